@@ -1,0 +1,256 @@
+"""Benchmark: int8 implicit-GEMM conv2d fprop on one MI355X.
+
+One step = one conv2d_fprop_run of the headline workload (int8 3x3 conv, N32
+C256 28x28 K256, stride 1, pad 1, NCxHWx<32> / CxRSKx<32>, fused alpha / rint /
+saturate epilogue) on inputs already resident in HBM.  Prints ONE JSON line.
+
+Secondary measurements (same line, key "extra"): microseconds per call of the
+smallest shape (device events, host wall clock, graph replay), the strided
+3x3 workload, the fp32 dilated workload and the layout transforms.  The CPU
+oracle is timed on the host as a reported baseline ("cpu_baseline").
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "int8 conv fprop TOPS (% of MFMA int8 peak); µs/call at smallest shape"
+PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 MFMA, 5.0 POP/s
+PEAK_FP32_TFLOPS = 157.3     # MI355X fp32 MFMA
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "conv_i8_c3_traffic.json")
+KERNEL_SOURCES = ["convolution_forward_gemm_amd/csrc/conv_i8.hip",
+                  "convolution_forward_gemm_amd/csrc/common.hpp",
+                  "convolution_forward_gemm_amd/csrc/api.hip"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def conv_ops(wk, P, Q) -> int:
+    return 2 * wk.N * wk.K * P * Q * wk.C * wk.R * wk.S
+
+
+def conv_bytes(wk, P, Q, esize) -> int:
+    return esize * (wk.N * wk.C * wk.H * wk.W + wk.K * wk.C * wk.R * wk.S + wk.N * wk.K * P * Q)
+
+
+def setup(wk, torch, b):
+    """Descriptor plus device-resident inputs/outputs in the kernel layouts."""
+    from convolution_forward_gemm_amd import workloads as wl
+    x, w = wl.make_inputs(wk)
+    conv = b.Conv2dFprop(wk.N, wk.C, wk.H, wk.W, wk.K, wk.R, wk.S, pad=wk.pad,
+                         stride=wk.stride, dil=wk.dil, dtype=wk.dtype)
+    if wk.dtype == "int8":
+        xd = b.nchw_to_nc32hw32(torch.from_numpy(x).cuda())
+        wd = b.kcrs_to_c32rsk32(torch.from_numpy(w).cuda())
+        yd = torch.empty(conv.y_shape, dtype=torch.int8, device="cuda")
+    else:
+        xd = torch.from_numpy(x).cuda()
+        wd = torch.from_numpy(w).cuda()
+        yd = torch.empty(conv.y_shape, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    return conv, xd, wd, yd, (x, w)
+
+
+def time_device(torch, fn, steps, warmup):
+    """Average device time per call (ms) with HIP events on the current stream."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        fn()
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps
+
+
+def latency_suite(torch, conv, xd, wd, yd, alpha, calls=1000):
+    """p5-style microseconds per call: device events, host wall, graph replay."""
+    stream = torch.cuda.current_stream().cuda_stream
+    xp, wp, yp = xd.data_ptr(), wd.data_ptr(), yd.data_ptr()
+
+    def call():
+        conv.run_ptr(xp, wp, yp, alpha, stream)
+
+    dev_ms = time_device(torch, call, calls, 50)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(calls):
+        call()
+    torch.cuda.synchronize()
+    host_us = (time.perf_counter() - t0) / calls * 1e6
+
+    graph_us = None
+    try:
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            gstream = torch.cuda.current_stream().cuda_stream
+            conv.run_ptr(xp, wp, yp, alpha, gstream)  # warm on the side stream
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=s):
+                cap = torch.cuda.current_stream().cuda_stream
+                for _ in range(20):
+                    conv.run_ptr(xp, wp, yp, alpha, cap)
+        torch.cuda.synchronize()
+        reps = 50
+        ms = time_device(torch, g.replay, reps, 5)
+        graph_us = ms * 1e3 / 20
+    except Exception as e:  # graph capture is a secondary measurement
+        graph_us = "unavailable: %s" % (type(e).__name__,)
+    return {"device_us_per_call": round(dev_ms * 1e3, 3),
+            "host_wall_us_per_call": round(host_us, 3),
+            "graph_replay_us_per_call": graph_us if isinstance(graph_us, str) else round(graph_us, 3)}
+
+
+def cpu_baseline(wk, x, w):
+    """The oracle as it stands, on the host cores (rank 0, N=1 only)."""
+    import oracle
+    threads = min(16, os.cpu_count() or 1)
+    try:
+        threads = min(threads, len(os.sched_getaffinity(0)))
+    except AttributeError:
+        pass
+    # Bounded sample: the first `n` images of the workload (all channels,
+    # all output pixels), about 10 s of CPU work at the expected rate.
+    n = max(1, min(wk.N, 8 * threads // 4))
+    t0 = time.perf_counter()
+    acc, y = oracle.conv2d_i8(x[:n], w, wk.alpha, **wk.conv_kwargs, nthreads=threads)
+    dt = time.perf_counter() - t0
+    P, Q = acc.shape[2:]
+    ops = 2 * n * wk.K * P * Q * wk.C * wk.R * wk.S
+    return {"value": round(ops / dt / 1e12, 6), "unit": "TOPS", "cores": threads,
+            "kind": "oracle",
+            "sample": "%d of %d images of the headline workload (all %d output channels, "
+                      "%dx%d outputs), int64 accumulation + epilogue; %.1f s"
+                      % (n, wk.N, wk.K, P, Q, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--no-extras", action="store_true", help="headline workload only")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--workload", default="c3", help="headline workload key (c3 default)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from convolution_forward_gemm_amd import binding as b
+    from convolution_forward_gemm_amd import workloads as wl
+
+    wk = wl.WORKLOADS[args.workload]
+    conv, xd, wd, yd, host_inputs = setup(wk, torch, b)
+    stream = torch.cuda.current_stream().cuda_stream
+    xp, wp, yp = xd.data_ptr(), wd.data_ptr(), yd.data_ptr()
+
+    def step():
+        conv.run_ptr(xp, wp, yp, wk.alpha, stream)
+
+    torch.cuda.synchronize()
+    ms = time_device(torch, step, args.steps, args.warmup)
+    ops = conv_ops(wk, conv.P, conv.Q)
+    tops = ops / (ms * 1e-3) / 1e12
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("kernel_source_hash") == kernel_source_hash() and tr.get("workload") == wk.key:
+            traffic = tr.get("hbm_bytes_per_launch")
+
+    out = {
+        "metric": METRIC,
+        "value": round(tops, 3),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic (seeded uniform int8, resident in HBM)",
+        "config": {"workload": wk.name, "N": wk.N, "C": wk.C, "H": wk.H, "W": wk.W,
+                   "K": wk.K, "R": wk.R, "S": wk.S, "pad": list(wk.pad),
+                   "stride": list(wk.stride), "dilation": list(wk.dil),
+                   "alpha": wk.alpha, "layout": "NCxHWx<32> / CxRSKx<32>",
+                   "kernel_config": conv.config, "pct_of_int8_peak": round(100 * tops / PEAK_INT8_TOPS, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(tops, 3), "peak": PEAK_INT8_TOPS,
+                     "unit": "TOPS", "frac": round(tops / PEAK_INT8_TOPS, 4),
+                     "traffic": traffic,
+                     "algorithmic_bytes_per_launch": conv_bytes(wk, conv.P, conv.Q, 1),
+                     "ops_per_launch": ops},
+    }
+
+    if not args.no_extras:
+        extra = {}
+        # smallest shape: microseconds per call
+        w1 = wl.WORKLOADS["c1"]
+        c1, x1, w1d, y1, _ = setup(w1, torch, b)
+        lat = latency_suite(torch, c1, x1, w1d, y1, w1.alpha)
+        lat["config"] = c1.config
+        lat["GBps_device"] = round(conv_bytes(w1, c1.P, c1.Q, 1) / (lat["device_us_per_call"] * 1e-6) / 1e9, 3)
+        extra["c1_smallest_us_per_call"] = lat
+        out["us_per_call_smallest"] = lat["device_us_per_call"]
+        w2 = wl.WORKLOADS["c2"]
+        c2, x2, w2d, y2, _ = setup(w2, torch, b)
+        lat2 = latency_suite(torch, c2, x2, w2d, y2, w2.alpha)
+        lat2["config"] = c2.config
+        extra["c2_1x1_us_per_call"] = lat2
+        # strided 3x3
+        w4 = wl.WORKLOADS["c4"]
+        c4, x4, w4d, y4, _ = setup(w4, torch, b)
+        s4 = torch.cuda.current_stream().cuda_stream
+        ms4 = time_device(torch, lambda: c4.run_ptr(x4.data_ptr(), w4d.data_ptr(), y4.data_ptr(), w4.alpha, s4), 500, 50)
+        t4 = conv_ops(w4, c4.P, c4.Q) / (ms4 * 1e-3) / 1e12
+        extra["c4_strided"] = {"ms": round(ms4, 6), "TOPS": round(t4, 3),
+                               "pct_of_int8_peak": round(100 * t4 / PEAK_INT8_TOPS, 2), "config": c4.config}
+        # transforms (GB/s, bytes read + written)
+        xs = torch.from_numpy(host_inputs[0]).cuda()
+        ilb = torch.empty((wk.N, wk.C // 32, wk.H, wk.W, 32), dtype=torch.int8, device="cuda")
+        lt = b.lib.conv_nchw_to_nc32hw32_i8
+        mst = time_device(torch, lambda: lt(xs.data_ptr(), ilb.data_ptr(), wk.N, wk.C, wk.H, wk.W, s4), 200, 20)
+        extra["transform_nchw_to_nc32hw32_c3x"] = {"ms": round(mst, 6),
+                                                   "GBps": round(2 * xs.numel() / (mst * 1e-3) / 1e9, 1)}
+        del xs, ilb
+        # fp32 dilated
+        w5 = wl.WORKLOADS["c5"]
+        c5, x5, w5d, y5, _ = setup(w5, torch, b)
+        ms5 = time_device(torch, lambda: c5.run_ptr(x5.data_ptr(), w5d.data_ptr(), y5.data_ptr(), 1.0, s4), 10, 2)
+        t5 = conv_ops(w5, c5.P, c5.Q) / (ms5 * 1e-3) / 1e12
+        extra["c5_fp32_dilated"] = {"ms": round(ms5, 4), "TFLOPS": round(t5, 3),
+                                    "pct_of_fp32_peak": round(100 * t5 / PEAK_FP32_TFLOPS, 2),
+                                    "config": c5.config}
+        out["extra"] = extra
+
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(wk, *host_inputs)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

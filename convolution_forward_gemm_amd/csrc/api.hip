@@ -1,0 +1,327 @@
+// api.hip -- the C ABI of libconvfprop.so (declared in include/convfprop.h).
+//
+// Host-side structure follows two lessons of the CUTLASS notebook "Best
+// practices for reducing host-side latency": validate and resolve the kernel
+// once ("Compile once, run many times", "Bypassing checks"), so that the run
+// call is a pointer check plus one kernel launch; and keep run free of
+// allocation, synchronisation and host copies so it can be captured into a
+// graph ("CUDA Graphs").  The operator shape (argument checks, then dispatch
+// of run-time types to compiled instantiations, then the kernel) is the one
+// the torchao PR 1515 review describes for CUTLASS-based operators.
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <new>
+
+#include "../../include/convfprop.h"
+#include "kernels.hpp"
+
+using namespace convfprop;
+
+struct conv2d_fprop_desc_s {
+  int N, C, H, W, K, R, S, ph, pw, sh, sw, dh, dw, P, Q;
+  conv_dtype_t dtype;
+  conv_layout_t layout;
+  int config;
+  int grid;
+  int64_t x_bytes, w_bytes, y_bytes;
+  I8Params i8;
+  F32Params f32;
+};
+
+namespace {
+
+constexpr int64_t kMaxTensorBytes = (int64_t(1) << 31) - 1;
+
+// floor((in + 2*pad - dil*(k-1) - 1) / stride) + 1, or <= 0 if nothing fits.
+int64_t out_extent(int64_t in, int64_t pad, int64_t dil, int64_t k, int64_t stride) {
+  const int64_t num = in + 2 * pad - dil * (k - 1) - 1;
+  if (num < 0) return 0;
+  return num / stride + 1;
+}
+
+bool ranges_overlap(const void *a, int64_t an, const void *b, int64_t bn) {
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + (uintptr_t)bn && b0 < a0 + (uintptr_t)an;
+}
+
+// Per-shape table: the configuration chosen for a problem by sweep.  Shapes
+// not listed fall back to the heuristic below.
+struct ShapeEntry {
+  conv_dtype_t dtype;
+  int N, C, H, W, K, R, S, ph, pw, sh, sw, dh, dw;
+  int config;
+};
+
+const ShapeEntry kShapeTable[] = {
+    {CONV_DTYPE_INT8, 1, 32, 8, 8, 32, 3, 3, 1, 1, 1, 1, 1, 1, 2},
+    {CONV_DTYPE_INT8, 2, 128, 8, 8, 128, 1, 1, 0, 0, 1, 1, 1, 1, 2},
+    {CONV_DTYPE_INT8, 32, 256, 28, 28, 256, 3, 3, 1, 1, 1, 1, 1, 1, 0},
+    {CONV_DTYPE_INT8, 32, 128, 56, 56, 256, 3, 3, 1, 1, 2, 2, 1, 1, 0},
+    {CONV_DTYPE_FP32, 8, 32, 512, 512, 64, 5, 9, 2, 4, 1, 1, 2, 3, 0},
+};
+
+int lookup_shape(const conv2d_fprop_desc_s &d) {
+  for (const ShapeEntry &e : kShapeTable)
+    if (e.dtype == d.dtype && e.N == d.N && e.C == d.C && e.H == d.H && e.W == d.W &&
+        e.K == d.K && e.R == d.R && e.S == d.S && e.ph == d.ph && e.pw == d.pw &&
+        e.sh == d.sh && e.sw == d.sw && e.dh == d.dh && e.dw == d.dw)
+      return e.config;
+  return -1;
+}
+
+int heuristic_i8(const conv2d_fprop_desc_s &d) {
+  const int64_t M = (int64_t)d.N * d.P * d.Q;
+  if (M * d.K <= 128 * 128) return 2;  // latency-bound: many small tiles
+  if (d.K <= 64) return 1;
+  return 0;
+}
+
+int heuristic_f32(const conv2d_fprop_desc_s &d) {
+  if (d.K <= 32) return 1;
+  return 0;
+}
+
+int f32_lds_bytes(const conv2d_fprop_desc_s &d, int cfg) {
+  return kF32Configs[cfg].lds_bytes * d.R * d.S;
+}
+
+// Fill the launch parameters for configuration `cfg`; false if it cannot run.
+bool plan(conv2d_fprop_desc_s &d, int cfg) {
+  const int64_t M = (int64_t)d.N * d.P * d.Q;
+  if (d.dtype == CONV_DTYPE_INT8) {
+    if (cfg < 0 || cfg >= kNumI8Configs) return false;
+    const I8Config &c = kI8Configs[cfg];
+    const int64_t mt = (M + c.bn - 1) / c.bn, kt = (d.K + c.bm - 1) / c.bm;
+    if (mt * kt > 0x7fffffff) return false;
+    I8Params &p = d.i8;
+    p.M = (int)M;
+    p.PQ = d.P * d.Q;
+    p.Q = d.Q;
+    p.H = d.H;
+    p.W = d.W;
+    p.HW = d.H * d.W;
+    p.CB = d.C / 32;
+    p.K = d.K;
+    p.KBLK = d.K / 32;
+    p.RS = d.R * d.S;
+    p.S = d.S;
+    p.ntaps = p.CB * p.RS;
+    p.ph = d.ph; p.pw = d.pw; p.sh = d.sh; p.sw = d.sw; p.dh = d.dh; p.dw = d.dw;
+    p.k_tiles = (int)kt;
+    p.x_bytes = (uint32_t)d.x_bytes;
+    p.w_bytes = (uint32_t)d.w_bytes;
+    p.alpha = 1.0f;
+    d.grid = (int)(mt * kt);
+  } else {
+    if (cfg < 0 || cfg >= kNumF32Configs) return false;
+    const F32Config &c = kF32Configs[cfg];
+    if (f32_lds_bytes(d, cfg) > 65536) return false;
+    const int64_t mt = (M + c.bn - 1) / c.bn, kt = (d.K + c.bm - 1) / c.bm;
+    if (mt * kt > 0x7fffffff) return false;
+    F32Params &p = d.f32;
+    p.M = (int)M;
+    p.PQ = d.P * d.Q;
+    p.Q = d.Q;
+    p.C = d.C;
+    p.H = d.H;
+    p.W = d.W;
+    p.HW = d.H * d.W;
+    p.K = d.K;
+    p.R = d.R;
+    p.S = d.S;
+    p.ph = d.ph; p.pw = d.pw; p.sh = d.sh; p.sw = d.sw; p.dh = d.dh; p.dw = d.dw;
+    p.k_tiles = (int)kt;
+    p.x_bytes = (uint32_t)d.x_bytes;
+    p.w_bytes = (uint32_t)d.w_bytes;
+    p.alpha = 1.0f;
+    d.grid = (int)(mt * kt);
+  }
+  d.config = cfg;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *conv_status_string(conv_status_t s) {
+  switch (s) {
+    case CONV_OK: return "CONV_OK: success";
+    case CONV_ERR_NULL: return "CONV_ERR_NULL: a required pointer is NULL";
+    case CONV_ERR_INVALID_SHAPE: return "CONV_ERR_INVALID_SHAPE: invalid sizes or empty output";
+    case CONV_ERR_UNSUPPORTED: return "CONV_ERR_UNSUPPORTED: problem not supported by this library";
+    case CONV_ERR_MISALIGNED: return "CONV_ERR_MISALIGNED: a pointer breaks the required alignment";
+    case CONV_ERR_OVERFLOW_RISK: return "CONV_ERR_OVERFLOW_RISK: C*R*S could overflow the int32 accumulator";
+    case CONV_ERR_HIP: return "CONV_ERR_HIP: the HIP runtime reported an error";
+    case CONV_ERR_NO_MEMORY: return "CONV_ERR_NO_MEMORY: host allocation failed";
+  }
+  return "unknown conv_status_t";
+}
+
+conv_status_t conv2d_fprop_desc_create(conv2d_fprop_desc_t *out, int N, int C,
+                                       int H, int W, int K, int R, int S,
+                                       int pad_h, int pad_w, int stride_h,
+                                       int stride_w, int dil_h, int dil_w,
+                                       conv_dtype_t dtype, conv_layout_t layout) {
+  if (!out) return CONV_ERR_NULL;
+  *out = nullptr;
+  if (N <= 0 || C <= 0 || H <= 0 || W <= 0 || K <= 0 || R <= 0 || S <= 0 ||
+      pad_h < 0 || pad_w < 0 || stride_h <= 0 || stride_w <= 0 || dil_h <= 0 ||
+      dil_w <= 0)
+    return CONV_ERR_INVALID_SHAPE;
+  const int64_t P = out_extent(H, pad_h, dil_h, R, stride_h);
+  const int64_t Q = out_extent(W, pad_w, dil_w, S, stride_w);
+  if (P < 1 || Q < 1) return CONV_ERR_INVALID_SHAPE;
+
+  int64_t esize;
+  if (dtype == CONV_DTYPE_INT8 && layout == CONV_LAYOUT_NC32HW32_C32RSK32) {
+    if (C % 32 != 0 || K % 32 != 0) return CONV_ERR_UNSUPPORTED;
+    // |acc| <= C*R*S * 128 * 128 must stay below 2^31.
+    if ((int64_t)C * R * S >= 131072) return CONV_ERR_OVERFLOW_RISK;
+    esize = 1;
+  } else if (dtype == CONV_DTYPE_FP32 && layout == CONV_LAYOUT_NCHW_KCRS) {
+    esize = 4;
+  } else {
+    return CONV_ERR_UNSUPPORTED;
+  }
+  const int64_t xb = (int64_t)N * C * H * W * esize;
+  const int64_t wb = (int64_t)K * C * R * S * esize;
+  const int64_t yb = (int64_t)N * K * P * Q * esize;
+  if (xb > kMaxTensorBytes || wb > kMaxTensorBytes || yb > kMaxTensorBytes)
+    return CONV_ERR_UNSUPPORTED;
+
+  conv2d_fprop_desc_s *d = new (std::nothrow) conv2d_fprop_desc_s();
+  if (!d) return CONV_ERR_NO_MEMORY;
+  d->N = N; d->C = C; d->H = H; d->W = W; d->K = K; d->R = R; d->S = S;
+  d->ph = pad_h; d->pw = pad_w; d->sh = stride_h; d->sw = stride_w;
+  d->dh = dil_h; d->dw = dil_w; d->P = (int)P; d->Q = (int)Q;
+  d->dtype = dtype;
+  d->layout = layout;
+  d->x_bytes = xb;
+  d->w_bytes = wb;
+  d->y_bytes = yb;
+
+  int cfg = lookup_shape(*d);
+  if (cfg < 0) cfg = dtype == CONV_DTYPE_INT8 ? heuristic_i8(*d) : heuristic_f32(*d);
+  bool ok = plan(*d, cfg);
+  if (!ok) {  // try every compiled configuration before giving up
+    const int n = dtype == CONV_DTYPE_INT8 ? kNumI8Configs : kNumF32Configs;
+    for (int c = 0; c < n && !ok; ++c) ok = plan(*d, c);
+  }
+  if (!ok) {
+    delete d;
+    return CONV_ERR_UNSUPPORTED;
+  }
+  *out = d;
+  return CONV_OK;
+}
+
+conv_status_t conv2d_fprop_desc_destroy(conv2d_fprop_desc_t desc) {
+  delete desc;
+  return CONV_OK;
+}
+
+conv_status_t conv2d_fprop_desc_get_output_dims(conv2d_fprop_desc_t d, int *P, int *Q) {
+  if (!d || !P || !Q) return CONV_ERR_NULL;
+  *P = d->P;
+  *Q = d->Q;
+  return CONV_OK;
+}
+
+conv_status_t conv2d_fprop_desc_get_config(conv2d_fprop_desc_t d, char *buf, size_t n) {
+  if (!d || !buf) return CONV_ERR_NULL;
+  if (n == 0) return CONV_OK;
+  const bool i8 = d->dtype == CONV_DTYPE_INT8;
+  const char *name = i8 ? kI8Configs[d->config].name : kF32Configs[d->config].name;
+  const int bm = i8 ? kI8Configs[d->config].bm : kF32Configs[d->config].bm;
+  const int bn = i8 ? kI8Configs[d->config].bn : kF32Configs[d->config].bn;
+  snprintf(buf, n, "config=%d %s tile=%dch x %dpx grid=%d", d->config, name, bm, bn,
+           d->grid);
+  return CONV_OK;
+}
+
+int conv2d_fprop_num_configs(conv_dtype_t dtype) {
+  if (dtype == CONV_DTYPE_INT8) return kNumI8Configs;
+  if (dtype == CONV_DTYPE_FP32) return kNumF32Configs;
+  return 0;
+}
+
+conv_status_t conv2d_fprop_desc_set_config(conv2d_fprop_desc_t d, int config) {
+  if (!d) return CONV_ERR_NULL;
+  conv2d_fprop_desc_s trial = *d;
+  if (!plan(trial, config)) return CONV_ERR_UNSUPPORTED;
+  *d = trial;
+  return CONV_OK;
+}
+
+conv_status_t conv2d_fprop_run(conv2d_fprop_desc_t d, const void *x, const void *w,
+                               void *y, float alpha, hipStream_t stream) {
+  if (!d || !x || !w || !y) return CONV_ERR_NULL;
+  const uintptr_t align = d->dtype == CONV_DTYPE_INT8 ? 16 : 4;
+  if (((uintptr_t)x | (uintptr_t)w | (uintptr_t)y) & (align - 1)) return CONV_ERR_MISALIGNED;
+  if (ranges_overlap(x, d->x_bytes, y, d->y_bytes) ||
+      ranges_overlap(w, d->w_bytes, y, d->y_bytes))
+    return CONV_ERR_UNSUPPORTED;
+  hipError_t e;
+  if (d->dtype == CONV_DTYPE_INT8) {
+    I8Params p = d->i8;
+    p.alpha = alpha;
+    e = kI8Configs[d->config].launch((const int8_t *)x, (const int8_t *)w, (int8_t *)y, p,
+                                     d->grid, stream);
+  } else {
+    F32Params p = d->f32;
+    p.alpha = alpha;
+    e = kF32Configs[d->config].launch((const float *)x, (const float *)w, (float *)y, p,
+                                      d->grid, stream);
+  }
+  return e == hipSuccess ? CONV_OK : CONV_ERR_HIP;
+}
+
+// ---- layout transforms ----------------------------------------------------
+static conv_status_t check_transform(const int8_t *src, int8_t *dst, int a, int C, int b,
+                                     int c) {
+  if (!src || !dst) return CONV_ERR_NULL;
+  if (a <= 0 || C <= 0 || b <= 0 || c <= 0) return CONV_ERR_INVALID_SHAPE;
+  if (C % 32 != 0) return CONV_ERR_UNSUPPORTED;
+  const int64_t bytes = (int64_t)a * C * b * c;
+  if (bytes > kMaxTensorBytes) return CONV_ERR_UNSUPPORTED;
+  if (((uintptr_t)src | (uintptr_t)dst) & 15) return CONV_ERR_MISALIGNED;
+  if (ranges_overlap(src, bytes, dst, bytes)) return CONV_ERR_UNSUPPORTED;
+  return CONV_OK;
+}
+
+conv_status_t conv_nchw_to_nc32hw32_i8(const int8_t *src, int8_t *dst, int N, int C,
+                                       int H, int W, hipStream_t stream) {
+  conv_status_t s = check_transform(src, dst, N, C, H, W);
+  if (s != CONV_OK) return s;
+  return launch_nchw_to_nc32(src, dst, N, C, H * W, stream) == hipSuccess ? CONV_OK
+                                                                           : CONV_ERR_HIP;
+}
+
+conv_status_t conv_nc32hw32_to_nchw_i8(const int8_t *src, int8_t *dst, int N, int C,
+                                       int H, int W, hipStream_t stream) {
+  conv_status_t s = check_transform(src, dst, N, C, H, W);
+  if (s != CONV_OK) return s;
+  return launch_nc32_to_nchw(src, dst, N, C, H * W, stream) == hipSuccess ? CONV_OK
+                                                                           : CONV_ERR_HIP;
+}
+
+conv_status_t conv_kcrs_to_c32rsk32_i8(const int8_t *src, int8_t *dst, int K, int C,
+                                       int R, int S, hipStream_t stream) {
+  conv_status_t s = check_transform(src, dst, K, C, R, S);
+  if (s != CONV_OK) return s;
+  return launch_kcrs_to_c32rsk(src, dst, K, C, R * S, stream) == hipSuccess ? CONV_OK
+                                                                             : CONV_ERR_HIP;
+}
+
+conv_status_t conv_c32rsk32_to_kcrs_i8(const int8_t *src, int8_t *dst, int K, int C,
+                                       int R, int S, hipStream_t stream) {
+  conv_status_t s = check_transform(src, dst, K, C, R, S);
+  if (s != CONV_OK) return s;
+  return launch_c32rsk_to_kcrs(src, dst, K, C, R * S, stream) == hipSuccess ? CONV_OK
+                                                                             : CONV_ERR_HIP;
+}
+
+}  // extern "C"

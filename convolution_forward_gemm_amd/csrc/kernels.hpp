@@ -1,0 +1,77 @@
+// kernels.hpp -- internal interface between the C ABI (api.hip) and the
+// kernel translation units.  Not installed; callers use include/convfprop.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace convfprop {
+
+// Problem constants of the int8 kernel, precomputed on the host once per
+// descriptor.  Byte counts are < 2^31 (checked at descriptor creation).
+struct I8Params {
+  int M;        // N*P*Q output pixels (GEMM M)
+  int PQ, Q;    // output plane size and width
+  int H, W, HW; // input height, width, plane size
+  int CB;       // C/32 input channel blocks
+  int K, KBLK;  // output channels and K/32
+  int RS, S;    // filter taps per channel block, filter width
+  int ntaps;    // CB*R*S reduction steps of 32 channels
+  int ph, pw, sh, sw, dh, dw;
+  int k_tiles;  // workgroup tiles along K
+  uint32_t x_bytes, w_bytes;
+  float alpha;
+};
+
+typedef hipError_t (*I8LaunchFn)(const int8_t *x, const int8_t *w, int8_t *y,
+                                 const I8Params &p, int grid, hipStream_t s);
+
+struct I8Config {
+  const char *name;
+  int bm;       // output channels per workgroup
+  int bn;       // output pixels per workgroup
+  int threads;
+  int lds_bytes;
+  I8LaunchFn launch;
+};
+
+// Host-only tables (not const: a const namespace-scope object would also be
+// emitted for the device and reference host launch functions).
+extern I8Config kI8Configs[];
+extern int kNumI8Configs;
+
+// Problem constants of the fp32 kernel.
+struct F32Params {
+  int M, PQ, Q;
+  int C, H, W, HW;
+  int K, R, S;
+  int ph, pw, sh, sw, dh, dw;
+  int k_tiles;
+  uint32_t x_bytes, w_bytes;
+  float alpha;
+};
+
+typedef hipError_t (*F32LaunchFn)(const float *x, const float *w, float *y,
+                                  const F32Params &p, int grid, hipStream_t s);
+
+struct F32Config {
+  const char *name;
+  int bm, bn, threads, lds_bytes;
+  int max_crs;  // largest C*R*S... 0 = unlimited
+  F32LaunchFn launch;
+};
+
+extern F32Config kF32Configs[];
+extern int kNumF32Configs;
+
+// Layout transforms (transforms.hip).
+hipError_t launch_nchw_to_nc32(const int8_t *src, int8_t *dst, int N, int C,
+                               int HW, hipStream_t s);
+hipError_t launch_nc32_to_nchw(const int8_t *src, int8_t *dst, int N, int C,
+                               int HW, hipStream_t s);
+hipError_t launch_kcrs_to_c32rsk(const int8_t *src, int8_t *dst, int K, int C,
+                                 int RS, hipStream_t s);
+hipError_t launch_c32rsk_to_kcrs(const int8_t *src, int8_t *dst, int K, int C,
+                                 int RS, hipStream_t s);
+
+}  // namespace convfprop

@@ -1,0 +1,143 @@
+/*
+ * convfprop.h -- C ABI of libconvfprop.so: 2D convolution forward (fprop)
+ * computed as an implicit GEMM on MI355X (gfx950).
+ *
+ * The operation (cross-correlation, zero padding, no filter flip):
+ *
+ *   acc[n][k][p][q] = sum_{c,r,s} X(n, c, p*stride_h - pad_h + r*dil_h,
+ *                                     q*stride_w - pad_w + s*dil_w) * w[k][c][r][s]
+ *
+ * with X = x inside the image and 0 outside, and output extents
+ *   P = floor((H + 2*pad_h - dil_h*(R-1) - 1) / stride_h) + 1   (Q likewise),
+ * the rule derived in the first turn of the POPCORNBENCH "Kimi-K2.6 l1_p80"
+ * transcript.  As a GEMM: M = N*P*Q output pixels, N = K output channels,
+ * reduction = C*R*S.
+ *
+ * Two paths are supported:
+ *
+ *   INT8 / NC32HW32_C32RSK32 -- the int8 kernel of CUTLASS issue 2996 ("How
+ *     to optimize cutlass int8 fprop2d kernel with NCxHWx interleaved layout"),
+ *     section "CUTLASS Kernel Configuration": int8 x int8 products, int32
+ *     accumulation, alpha-only fp32 scaling and a clamp to int8:
+ *       y = clamp(rint(fl32(fl32(acc) * alpha)), -128, 127)
+ *     (one int32->fp32 conversion, one fp32 multiply, round half to even).
+ *     Memory layouts, all int8, dense, no padding between elements:
+ *       x: NCxHWx<32>  = [N][C/32][H][W][32]
+ *       w: CxRSKx<32>  = [C/32][R][S][K][32]
+ *       y: NCxHWx<32>  = [N][K/32][P][Q][32]
+ *     C and K must be multiples of 32.
+ *
+ *   FP32 / NCHW_KCRS -- the general fp32 case of the transcript (stride,
+ *     dilation, per-dimension padding): x NCHW fp32, w KCRS fp32
+ *     ([K][C][R][S]), y NKPQ fp32, y = alpha * acc with fp32 accumulation.
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers x, w, y, src, dst are DEVICE pointers owned by the caller; the
+ *     library never allocates, frees or copies them.  x/w/src are read only.
+ *   - `stream` is a HIP stream (0 = the null stream).  Every call only
+ *     enqueues work on it and returns; nothing synchronises, allocates device
+ *     memory or copies between host and device, so calls may be captured in a
+ *     HIP graph.  Completion is observed by the caller (stream/event sync).
+ *   - Errors are return codes; no call aborts, throws or prints.  When a call
+ *     returns an error, nothing was enqueued and outputs are untouched.
+ *   - Each tensor must be smaller than 2^31 bytes (32-bit buffer offsets).
+ */
+#ifndef CONVFPROP_H
+#define CONVFPROP_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    CONV_OK = 0,
+    CONV_ERR_NULL = 1,           /* a required pointer is NULL                    */
+    CONV_ERR_INVALID_SHAPE = 2,  /* a size <= 0, a pad < 0, or no output position */
+    CONV_ERR_UNSUPPORTED = 3,    /* valid problem this library does not handle   */
+    CONV_ERR_MISALIGNED = 4,     /* a device pointer breaks the required alignment */
+    CONV_ERR_OVERFLOW_RISK = 5,  /* int8 C*R*S could overflow the int32 accumulator */
+    CONV_ERR_HIP = 6,            /* the HIP runtime reported an error on launch   */
+    CONV_ERR_NO_MEMORY = 7       /* host allocation of the descriptor failed      */
+} conv_status_t;
+
+typedef enum { CONV_DTYPE_INT8 = 0, CONV_DTYPE_FP32 = 1 } conv_dtype_t;
+
+typedef enum {
+    CONV_LAYOUT_NCHW_KCRS = 0,          /* fp32 path                   */
+    CONV_LAYOUT_NC32HW32_C32RSK32 = 1   /* int8 path, interleaved x32  */
+} conv_layout_t;
+
+/* Opaque, immutable problem descriptor ("compile once, run many times":
+ * all validation and kernel selection happen at creation, as the CUTLASS
+ * host-latency notes recommend).  A descriptor may be used by concurrent
+ * run calls on different streams. */
+typedef struct conv2d_fprop_desc_s *conv2d_fprop_desc_t;
+
+/* Validate a problem and choose its kernel configuration.
+ *   out         receives the descriptor (set to NULL on error)
+ *   N,C,H,W     input batch, channels, height, width        (> 0)
+ *   K,R,S       output channels, filter height, filter width (> 0)
+ *   pad_*       zero padding applied to both sides           (>= 0)
+ *   stride_*, dil_*                                           (> 0)
+ * Supported (dtype, layout): (INT8, NC32HW32_C32RSK32) with C % 32 == 0,
+ * K % 32 == 0 and C*R*S < 131072 (so |acc| <= C*R*S*128*128 < 2^31), and
+ * (FP32, NCHW_KCRS).  Returns CONV_ERR_INVALID_SHAPE if P or Q < 1. */
+conv_status_t conv2d_fprop_desc_create(conv2d_fprop_desc_t *out, int N, int C,
+                                       int H, int W, int K, int R, int S,
+                                       int pad_h, int pad_w, int stride_h,
+                                       int stride_w, int dil_h, int dil_w,
+                                       conv_dtype_t dtype, conv_layout_t layout);
+
+/* Release a descriptor.  NULL is accepted and ignored. */
+conv_status_t conv2d_fprop_desc_destroy(conv2d_fprop_desc_t desc);
+
+/* Output extents P (rows) and Q (columns) of a descriptor. */
+conv_status_t conv2d_fprop_desc_get_output_dims(conv2d_fprop_desc_t desc,
+                                                int *P, int *Q);
+
+/* NUL-terminated text naming the chosen kernel configuration (tile shape,
+ * stages, launch grid), truncated to buf_size bytes. */
+conv_status_t conv2d_fprop_desc_get_config(conv2d_fprop_desc_t desc, char *buf,
+                                           size_t buf_size);
+
+/* Number of kernel configurations compiled for a dtype, and a replacement of
+ * a descriptor's configuration by index (for sweeps).  Returns
+ * CONV_ERR_UNSUPPORTED if that configuration cannot run the problem. */
+int conv2d_fprop_num_configs(conv_dtype_t dtype);
+conv_status_t conv2d_fprop_desc_set_config(conv2d_fprop_desc_t desc, int config);
+
+/* Enqueue one convolution on `stream`.
+ *   x     device input  (layout per the descriptor)
+ *   w     device filter (layout per the descriptor)
+ *   y     device output (layout per the descriptor); fully overwritten
+ *   alpha output scale (int8: applied before rounding; fp32: y = alpha*acc)
+ * The int8 path needs x, w and y 16-byte aligned; the fp32 path 4-byte.
+ * x and w must not overlap y. */
+conv_status_t conv2d_fprop_run(conv2d_fprop_desc_t desc, const void *x,
+                               const void *w, void *y, float alpha,
+                               hipStream_t stream);
+
+/* Layout transforms (pure permutations, int8).  C must be a multiple of 32.
+ * src and dst must not overlap; both 16-byte aligned.
+ *   NCHW [N][C][H][W]          <-> NCxHWx<32> [N][C/32][H][W][32]
+ *   KCRS [K][C][R][S]          <-> CxRSKx<32> [C/32][R][S][K][32]        */
+conv_status_t conv_nchw_to_nc32hw32_i8(const int8_t *src, int8_t *dst, int N,
+                                       int C, int H, int W, hipStream_t stream);
+conv_status_t conv_nc32hw32_to_nchw_i8(const int8_t *src, int8_t *dst, int N,
+                                       int C, int H, int W, hipStream_t stream);
+conv_status_t conv_kcrs_to_c32rsk32_i8(const int8_t *src, int8_t *dst, int K,
+                                       int C, int R, int S, hipStream_t stream);
+conv_status_t conv_c32rsk32_to_kcrs_i8(const int8_t *src, int8_t *dst, int K,
+                                       int C, int R, int S, hipStream_t stream);
+
+/* Static description of a status code (never NULL). */
+const char *conv_status_string(conv_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CONVFPROP_H */

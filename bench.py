@@ -151,6 +151,9 @@ def main():
     ap.add_argument("--no-extras", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--workload", default="c3", help="headline workload key (c3 default)")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="after the timed region, run a plain device copy of this many MiB "
+                         "(three times) to calibrate rocprofv3 FETCH_SIZE / WRITE_SIZE")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -246,6 +249,17 @@ def main():
                                     "pct_of_fp32_peak": round(100 * t5 / PEAK_FP32_TFLOPS, 2),
                                     "config": c5.config}
         out["extra"] = extra
+
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["calib_copy_bytes"] = n
+        del src, dst
 
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(wk, *host_inputs)

@@ -13,6 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libconvfprop.so")
+PEAK_PROBE = os.path.join(PKG, "peak_probe")
 SOURCES = ["api.hip", "conv_i8.hip", "conv_f32.hip", "transforms.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -27,10 +28,7 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, *FLAGS, *srcs, "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -40,9 +38,25 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed (%d):\n%s" % (res.returncode, err))
     if err.strip() and verbose:
         print(err, file=sys.stderr)
+
+
+def build_peak_probe(verbose: bool = False) -> str:
+    """The throughput-ceiling probe (an executable, not part of the library)."""
+    tmp = PEAK_PROBE + ".tmp%d" % os.getpid()
+    flags = [f for f in FLAGS if f not in ("-fPIC", "-shared")]
+    _run([HIPCC, *flags, os.path.join(CSRC, "peak_probe.hip"), "-o", tmp], verbose)
+    os.replace(tmp, PEAK_PROBE)
+    return PEAK_PROBE
+
+
+def build(verbose: bool = False) -> str:
+    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    tmp = LIB + ".tmp%d" % os.getpid()
+    _run([HIPCC, *FLAGS, *srcs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 
 
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_peak_probe(verbose=True))

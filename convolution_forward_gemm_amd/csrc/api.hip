@@ -14,7 +14,7 @@
 
 #include <new>
 
-#include "../../include/convfprop.h"
+#include "convfprop.h"
 #include "kernels.hpp"
 
 using namespace convfprop;
@@ -55,10 +55,14 @@ struct ShapeEntry {
 };
 
 const ShapeEntry kShapeTable[] = {
-    {CONV_DTYPE_INT8, 1, 32, 8, 8, 32, 3, 3, 1, 1, 1, 1, 1, 1, 2},
-    {CONV_DTYPE_INT8, 2, 128, 8, 8, 128, 1, 1, 0, 0, 1, 1, 1, 1, 2},
-    {CONV_DTYPE_INT8, 32, 256, 28, 28, 256, 3, 3, 1, 1, 1, 1, 1, 1, 0},
-    {CONV_DTYPE_INT8, 32, 128, 56, 56, 256, 3, 3, 1, 1, 2, 2, 1, 1, 0},
+    // int8 3x3 N1 C32 8x8 K32: launch-latency bound, one 32x32 tile per wave
+    {CONV_DTYPE_INT8, 1, 32, 8, 8, 32, 3, 3, 1, 1, 1, 1, 1, 1, 3},
+    // int8 1x1 N2 C128 8x8 K128 (a 128x128x128 GEMM): many small tiles
+    {CONV_DTYPE_INT8, 2, 128, 8, 8, 128, 1, 1, 0, 0, 1, 1, 1, 1, 14},
+    // int8 3x3 N32 C256 28x28 K256 and the stride-2 N32 C128 56x56 K256:
+    // 128 ch x 256 px tiles, 8 waves, 4 taps per stage, (r, s)-outer
+    {CONV_DTYPE_INT8, 32, 256, 28, 28, 256, 3, 3, 1, 1, 1, 1, 1, 1, 13},
+    {CONV_DTYPE_INT8, 32, 128, 56, 56, 256, 3, 3, 1, 1, 2, 2, 1, 1, 13},
     {CONV_DTYPE_FP32, 8, 32, 512, 512, 64, 5, 9, 2, 4, 1, 1, 2, 3, 0},
 };
 
@@ -73,9 +77,11 @@ int lookup_shape(const conv2d_fprop_desc_s &d) {
 
 int heuristic_i8(const conv2d_fprop_desc_s &d) {
   const int64_t M = (int64_t)d.N * d.P * d.Q;
-  if (M * d.K <= 128 * 128) return 2;  // latency-bound: many small tiles
-  if (d.K <= 64) return 1;
-  return 0;
+  const int cb = d.C / 32;
+  if (M * d.K <= 128 * 128) return cb % 2 == 0 ? 14 : 3;  // latency-bound: small tiles
+  if (cb % 4 == 0) return 13;                             // (r, s)-outer, 4 taps per stage
+  if (cb % 2 == 0) return 11;                             // (r, s)-outer, 2 taps per stage
+  return 0;                                               // generic tap order
 }
 
 int heuristic_f32(const conv2d_fprop_desc_s &d) {
@@ -93,6 +99,7 @@ bool plan(conv2d_fprop_desc_s &d, int cfg) {
   if (d.dtype == CONV_DTYPE_INT8) {
     if (cfg < 0 || cfg >= kNumI8Configs) return false;
     const I8Config &c = kI8Configs[cfg];
+    if (c.rs_outer && (d.C / 32) % c.kt != 0) return false;
     const int64_t mt = (M + c.bn - 1) / c.bn, kt = (d.K + c.bm - 1) / c.bm;
     if (mt * kt > 0x7fffffff) return false;
     I8Params &p = d.i8;
@@ -105,8 +112,9 @@ bool plan(conv2d_fprop_desc_s &d, int cfg) {
     p.CB = d.C / 32;
     p.K = d.K;
     p.KBLK = d.K / 32;
-    p.RS = d.R * d.S;
+    p.R = d.R;
     p.S = d.S;
+    p.RS = d.R * d.S;
     p.ntaps = p.CB * p.RS;
     p.ph = d.ph; p.pw = d.pw; p.sh = d.sh; p.sw = d.sw; p.dh = d.dh; p.dw = d.dw;
     p.k_tiles = (int)kt;

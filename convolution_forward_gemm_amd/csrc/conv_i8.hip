@@ -38,7 +38,7 @@
 
 namespace convfprop {
 
-template <int WK, int WP, int FK, int FP, int KT>
+template <int WK, int WP, int FK, int FP, int KT, int NS>
 struct I8Tile {
   static constexpr int NWAVES = WK * WP;
   static constexpr int THREADS = 64 * NWAVES;
@@ -46,17 +46,21 @@ struct I8Tile {
   static constexpr int PB = WP * FP;  // 32-pixel blocks per workgroup
   static constexpr int BM = 32 * KB;  // output channels per workgroup
   static constexpr int BN = 32 * PB;  // output pixels per workgroup
-  // Blocks of one stage handled per wave (filter and pixel side).
+  // Blocks of one stage are split over the waves (filter and pixel side).
+  static_assert(KT % 2 == 0, "fragment double-buffering needs an even tap count per stage");
+  static_assert(NS >= 3, "the ring needs a stage being read, one landed and one in flight");
   static_assert((KB * KT) % NWAVES == 0, "filter blocks must split over waves");
   static_assert((PB * KT) % NWAVES == 0, "pixel blocks must split over waves");
   static_assert(KB >= NWAVES ? KB % NWAVES == 0 : (NWAVES % KB == 0 && KT % (NWAVES / KB) == 0), "filter split");
   static_assert(PB >= NWAVES ? PB % NWAVES == 0 : (NWAVES % PB == 0 && KT % (NWAVES / PB) == 0), "pixel split");
-  static constexpr int WLOADS = KB * KT / NWAVES;
-  static constexpr int XLOADS = PB * KT / NWAVES;
+  static constexpr int WLOADS = KB * KT / NWAVES;   // 1 KiB filter blocks per wave per stage
+  static constexpr int XLOADS = PB * KT / NWAVES;   // 1 KiB pixel blocks per wave per stage
+  static constexpr int NL = WLOADS + XLOADS;        // LDS-DMA instructions per wave per stage
+  static_assert(NL * (NS - 2) < 64, "vmcnt counts at most 63 outstanding loads");
   static constexpr int NPX = PB >= NWAVES ? PB / NWAVES : 1;  // distinct pixels per lane
   static constexpr int NKC = KB >= NWAVES ? KB / NWAVES : 1;  // distinct channels per lane
   static constexpr int STAGE_BYTES = (KB + PB) * KT * 1024;
-  static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
+  static constexpr int LDS_BYTES = NS * STAGE_BYTES;
 };
 
 // Which (block, tap-in-stage) a wave's j-th load of a stage covers.
@@ -75,11 +79,93 @@ __device__ __forceinline__ void split_block(int wave, int j, int &blk_slot, int 
   }
 }
 
-template <int WK, int WP, int FK, int FP, int KT>
+// s_waitcnt with vmcnt(VM), lgkmcnt(0), expcnt untouched (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+template <int VM>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | ((VM >> 4) << 14));
+}
+
+// Workgroup barrier WITHOUT the release/acquire fence of __syncthreads():
+// that fence would make the compiler drain every outstanding load (vmcnt(0))
+// and so empty the LDS ring.  Visibility of LDS data is established by the
+// explicit waits before it; the empty asm keeps the compiler from moving
+// memory operations across.
+__device__ __forceinline__ void ring_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Increments of the activation tap offset when the filter position moves
+// by one tap: along S, at the end of a filter row, at the end of a channel
+// block.  Offsets are bytes into NCxHWx<32> relative to the pixel's origin.
+struct TapSteps {
+  int S, R, dh, dw;
+  int ds, dr, dcb;  // xoff increments: next s, row wrap, channel-block wrap
+};
+
+__device__ __forceinline__ TapSteps make_tap_steps(const I8Params &p) {
+  TapSteps t;
+  t.S = p.S;
+  t.R = p.R;
+  t.dh = p.dh;
+  t.dw = p.dw;
+  t.ds = 32 * p.dw;
+  t.dr = 32 * (p.dh * p.W - p.S * p.dw);
+  t.dcb = 32 * (p.HW - p.R * p.dh * p.W);
+  return t;
+}
+
+// Wave-uniform position in the tap sequence t = (cb, r, s), s fastest (the
+// tap order of CxRSKx<32>).  Stepping is branch-free: increments and selects.
+struct TapWalker {
+  int tap, s, r, rdh, sdw, xoff;  // xoff = 32*(cb*HW + r*dh*W + s*dw)
+  __device__ __forceinline__ void reset() { tap = s = r = rdh = sdw = xoff = 0; }
+  __device__ __forceinline__ void step(const TapSteps &k) {
+    ++tap;
+    ++s;
+    sdw += k.dw;
+    xoff += k.ds;
+    const bool ws = s == k.S;
+    s = ws ? 0 : s;
+    sdw = ws ? 0 : sdw;
+    r += ws ? 1 : 0;
+    rdh += ws ? k.dh : 0;
+    xoff += ws ? k.dr : 0;
+    const bool wr = r == k.R;
+    r = wr ? 0 : r;
+    rdh = wr ? 0 : rdh;
+    xoff += wr ? k.dcb : 0;
+  }
+};
+
+// What a stage's loads need to know about one of its taps.
+struct TapDesc {
+  int live;  // tap < ntaps
+  int rdh, sdw, xoff;
+};
+
+template <int KT>
+__device__ __forceinline__ TapDesc pick_tap(const TapDesc (&td)[KT], int t) {
+  TapDesc d = td[0];
+#pragma unroll
+  for (int i = 1; i < KT; ++i)
+    if (t == i) d = td[i];  // folds away when t is a compile-time constant
+  return d;
+}
+
+// RSO selects the reduction order.  false: taps t = (cb, r, s), s fastest,
+// any shape (a wave-uniform walker tracks the tap).  true: (r, s) outer and
+// the channel block inner, which needs C/32 % KT == 0: every stage then has a
+// single filter position, so the padding mask is evaluated once per stage and
+// the KT loads of a lane differ only in a wave-uniform offset.
+template <int WK, int WP, int FK, int FP, int KT, int NS, bool RSO>
 __global__ void __launch_bounds__(64 * WK * WP)
 conv_i8_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ w,
                int8_t *__restrict__ y, I8Params p) {
-  using T = I8Tile<WK, WP, FK, FP, KT>;
+  using T = I8Tile<WK, WP, FK, FP, KT, NS>;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
 
   const int tid = threadIdx.x;
@@ -121,74 +207,141 @@ conv_i8_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ w,
     }
   }
   // ---- per-lane filter channel (fixed across taps) -----------------------
-  int wk_off[T::NKC];
-  bool wk_ok[T::NKC];
+  // The lane's offset within a tap's K x 32 block; channels past K read zeros.
+  uint32_t wv[T::NKC];
 #pragma unroll
   for (int i = 0; i < T::NKC; ++i) {
     int kb = (T::KB >= T::NWAVES) ? wave + T::NWAVES * i : wave % T::KB;
     int k = k0 + 32 * kb + l32;
-    wk_ok[i] = k < p.K;
-    wk_off[i] = k * 32 + 16 * half;
+    wv[i] = k < p.K ? (uint32_t)(k * 32 + 16 * half) : OOB_OFFSET;
   }
 
   const int ntaps = p.ntaps;
   const int nstages = (ntaps + KT - 1) / KT;
   const int tap_stride_w = p.K * 32;  // bytes between consecutive taps of w
+  const int HW32 = p.HW * 32;         // bytes between channel blocks of x
 
-  v4i xbuf[T::XLOADS];
-  v4i wbuf[T::WLOADS];
-
-  // Tap t -> (cb, r, s) with s fastest, matching CxRSKx<32>'s tap order.
-  auto issue_loads = [&](int stage) {
-#pragma unroll
-    for (int j = 0; j < T::XLOADS; ++j) {
-      int slot, blk, t;
-      split_block<T::PB, T::NWAVES, KT>(wave, j, slot, blk, t);
-      int tap = stage * KT + t;
-      uint32_t off = OOB_OFFSET;
-      if (tap < ntaps) {
-        int cb = tap / p.RS;
-        int rs = tap - cb * p.RS;
-        int r = rs / p.S;
-        int s = rs - r * p.S;
-        int h = px_h0[slot] + r * p.dh;
-        int ww = px_w0[slot] + s * p.dw;
-        if ((unsigned)h < (unsigned)p.H && (unsigned)ww < (unsigned)p.W)
-          off = (uint32_t)(px_base[slot] + (cb * p.HW + r * p.dh * p.W + s * p.dw) * 32);
-      }
-      xbuf[j] = load_b128(xr, off);
-    }
-#pragma unroll
-    for (int j = 0; j < T::WLOADS; ++j) {
-      int slot, blk, t;
-      split_block<T::KB, T::NWAVES, KT>(wave, j, slot, blk, t);
-      int tap = stage * KT + t;
-      uint32_t off = OOB_OFFSET;
-      if (tap < ntaps && wk_ok[slot]) off = (uint32_t)(tap * tap_stride_w + wk_off[slot]);
-      wbuf[j] = load_b128(wr, off);
-    }
+  // Global -> LDS loads (LDS-DMA) of one stage into ring slot stage % NS.
+  // Each instruction moves one 1 KiB fragment block: lane l's 16 bytes land
+  // at block + 16*l, which is the MFMA operand order.  The per-lane part of
+  // the address is the voffset, a wave-uniform part may go in the soffset.
+  // Padded taps, pixels past M and channels past K use OOB_OFFSET as voffset
+  // and the buffer unit writes zeros.  The range check sees voffset only, so
+  // every in-range access must have a non-negative voffset of its own.
+  // soff is wave-uniform by construction; readfirstlane states it so that the
+  // compiler keeps it in an SGPR instead of wrapping the load in a loop.
+  auto dma = [&](__amdgpu_buffer_rsrc_t r, unsigned char *dst, uint32_t voff, int soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (__attribute__((address_space(3))) void *)dst, 16, voff,
+        __builtin_amdgcn_readfirstlane(soff), 0, 0);
   };
 
-  // LDS stage layout: [filter: t][kb][lane] then [pixels: t][pb][lane], 16 B each.
-  auto store_stage = [&](int buf) {
-    unsigned char *base = lds + buf * T::STAGE_BYTES;
-#pragma unroll
-    for (int j = 0; j < T::WLOADS; ++j) {
-      int slot, blk, t;
-      split_block<T::KB, T::NWAVES, KT>(wave, j, slot, blk, t);
-      *reinterpret_cast<v4i *>(base + ((t * T::KB + blk) * 64 + lane) * 16) = wbuf[j];
-    }
+  // (cb, r, s) walker state for the generic order.
+  const TapSteps steps = make_tap_steps(p);
+  TapWalker walker;
+  walker.reset();
+  // (r, s)-outer state: the next stage's first channel block and position.
+  int ld_cb0 = 0, ld_rs = 0, ld_s = 0, ld_rdh = 0, ld_sdw = 0, ld_xrs = 0;
+
+  // Stages past the end are still issued, with every lane out of range: they
+  // zero-fill the slot of an already consumed stage.  This keeps the loop body
+  // free of branches (so the scheduler can interleave it) and the wait counts
+  // exact.  An out-of-range voffset makes the whole access out of range, so
+  // no address past a buffer is ever formed.
+  auto load_next_stage = [&](int stage) {
+    unsigned char *base = lds + (stage % NS) * T::STAGE_BYTES;
     unsigned char *xb = base + T::KB * KT * 1024;
+    const bool live = stage < nstages;
+    if constexpr (RSO) {
+      uint32_t xv[T::NPX];  // this stage's padding decision per pixel
 #pragma unroll
-    for (int j = 0; j < T::XLOADS; ++j) {
-      int slot, blk, t;
-      split_block<T::PB, T::NWAVES, KT>(wave, j, slot, blk, t);
-      *reinterpret_cast<v4i *>(xb + ((t * T::PB + blk) * 64 + lane) * 16) = xbuf[j];
+      for (int i = 0; i < T::NPX; ++i) {
+        const int h = px_h0[i] + ld_rdh;
+        const int ww = px_w0[i] + ld_sdw;
+        // The filter-position part goes into voffset: the buffer range check
+        // applies to voffset alone, and a padded pixel's origin (h0 or w0 < 0)
+        // is a negative offset that only the in-image tap makes valid.
+        xv[i] = (live && (unsigned)h < (unsigned)p.H && (unsigned)ww < (unsigned)p.W)
+                    ? (uint32_t)(px_base[i] + ld_xrs)
+                    : OOB_OFFSET;
+      }
+#pragma unroll
+      for (int j = 0; j < T::XLOADS; ++j) {
+        int slot, blk, t;
+        split_block<T::PB, T::NWAVES, KT>(wave, j, slot, blk, t);
+        dma(xr, xb + (t * T::PB + blk) * 1024, xv[slot], (ld_cb0 + t) * HW32);
+      }
+#pragma unroll
+      for (int j = 0; j < T::WLOADS; ++j) {
+        int slot, blk, t;
+        split_block<T::KB, T::NWAVES, KT>(wave, j, slot, blk, t);
+        dma(wr, base + (t * T::KB + blk) * 1024, live ? wv[slot] : OOB_OFFSET,
+            live ? ((ld_cb0 + t) * p.RS + ld_rs) * tap_stride_w : 0);
+      }
+      // advance by KT channel blocks; at the end of the blocks, to the next
+      // filter position (selects, not branches: the body stays one block)
+      ld_cb0 += KT;
+      const bool wrap_cb = ld_cb0 == p.CB;
+      ld_cb0 = wrap_cb ? 0 : ld_cb0;
+      ld_rs += wrap_cb ? 1 : 0;
+      ld_s += wrap_cb ? 1 : 0;
+      ld_sdw += wrap_cb ? p.dw : 0;
+      ld_xrs += wrap_cb ? 32 * p.dw : 0;
+      const bool wrap_s = ld_s == p.S;
+      ld_s = wrap_s ? 0 : ld_s;
+      ld_sdw = wrap_s ? 0 : ld_sdw;
+      ld_rdh += wrap_s ? p.dh : 0;
+      ld_xrs += wrap_s ? 32 * (p.dh * p.W - p.S * p.dw) : 0;
+    } else {
+      TapDesc td[KT];
+#pragma unroll
+      for (int t = 0; t < KT; ++t) {
+        td[t].live = walker.tap < ntaps;
+        td[t].rdh = walker.rdh;
+        td[t].sdw = walker.sdw;
+        td[t].xoff = walker.xoff;
+        walker.step(steps);
+      }
+#pragma unroll
+      for (int j = 0; j < T::XLOADS; ++j) {
+        int slot, blk, t;
+        split_block<T::PB, T::NWAVES, KT>(wave, j, slot, blk, t);
+        const TapDesc d = pick_tap<KT>(td, t);
+        const int h = px_h0[slot] + d.rdh;
+        const int ww = px_w0[slot] + d.sdw;
+        const bool ok = d.live && (unsigned)h < (unsigned)p.H && (unsigned)ww < (unsigned)p.W;
+        dma(xr, xb + (t * T::PB + blk) * 1024,
+            ok ? (uint32_t)(px_base[slot] + d.xoff) : OOB_OFFSET, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < T::WLOADS; ++j) {
+        int slot, blk, t;
+        split_block<T::KB, T::NWAVES, KT>(wave, j, slot, blk, t);
+        // Taps past the reduction read tap 0's filter: their activations
+        // are zero, so the product is zero either way.
+        const int tap = stage * KT + t;
+        dma(wr, base + (t * T::KB + blk) * 1024, live ? wv[slot] : OOB_OFFSET,
+            tap < ntaps ? tap * tap_stride_w : 0);
+      }
     }
   };
 
   const int wk = wave % WK;  // this wave's channel sub-tile
   const int wp = wave / WK;  // this wave's pixel sub-tile
+
+  // MFMA operand fragments, double-buffered across taps so the LDS reads of
+  // tap t+1 are in flight while the MFMAs of tap t run.
+  v4i af[2][FK], bf[2][FP];
+  auto read_frags = [&](int stage, int t, v4i (&a)[FK], v4i (&b)[FP]) {
+    const unsigned char *base = lds + (stage % NS) * T::STAGE_BYTES;
+    const unsigned char *xb = base + T::KB * KT * 1024;
+#pragma unroll
+    for (int i = 0; i < FK; ++i)
+      a[i] = *reinterpret_cast<const v4i *>(base + ((t * T::KB + wk * FK + i) * 64 + lane) * 16);
+#pragma unroll
+    for (int i = 0; i < FP; ++i)
+      b[i] = *reinterpret_cast<const v4i *>(xb + ((t * T::PB + wp * FP + i) * 64 + lane) * 16);
+  };
 
   v16i acc[FK][FP];
 #pragma unroll
@@ -196,35 +349,49 @@ conv_i8_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ w,
 #pragma unroll
     for (int b = 0; b < FP; ++b) acc[a][b] = v16i{0};
 
-  issue_loads(0);
-  store_stage(0);
-  __syncthreads();
+  // Ring schedule.  Barrier B_k (all waves) certifies that stage k has landed
+  // and that every wave has finished reading stage k-2; after it, the slot of
+  // stage k-2 is refilled with stage k-2+NS.  B_{s+1} sits just before the
+  // last tap of stage s, so the first fragments of stage s+1 are read while
+  // that tap's MFMAs run.
+#pragma unroll
+  for (int s0 = 0; s0 < NS - 1; ++s0) load_next_stage(s0);
+  wait_vm_lgkm0<T::NL * (NS - 2)>();  // stage 0 landed
+  ring_barrier();
+  read_frags(0, 0, af[0], bf[0]);
 
   for (int st = 0; st < nstages; ++st) {
-    const int cur = st & 1;
-    const bool more = st + 1 < nstages;
-    if (more) issue_loads(st + 1);
-
-    const unsigned char *base = lds + cur * T::STAGE_BYTES;
-    const unsigned char *xb = base + T::KB * KT * 1024;
 #pragma unroll
     for (int t = 0; t < KT; ++t) {
-      v4i af[FK], bf[FP];
-#pragma unroll
-      for (int a = 0; a < FK; ++a)
-        af[a] = *reinterpret_cast<const v4i *>(base + ((t * T::KB + wk * FK + a) * 64 + lane) * 16);
-#pragma unroll
-      for (int b = 0; b < FP; ++b)
-        bf[b] = *reinterpret_cast<const v4i *>(xb + ((t * T::PB + wp * FP + b) * 64 + lane) * 16);
+      if (t + 1 < KT) {
+        read_frags(st, t + 1, af[(t + 1) & 1], bf[(t + 1) & 1]);
+      } else {
+        // stage st+1 landed: all but the NS-3 newest stages are complete
+        wait_vm_lgkm0<T::NL * (NS - 3)>();
+        ring_barrier();
+        load_next_stage(st + NS - 1);          // into the slot of stage st-1
+        read_frags(st + 1, 0, af[0], bf[0]);  // KT is even: tap 0 -> buffer 0
+      }
 #pragma unroll
       for (int a = 0; a < FK; ++a)
 #pragma unroll
         for (int b = 0; b < FP; ++b)
-          acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[a], bf[b], acc[a][b], 0, 0, 0);
+          acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[t & 1][a], bf[t & 1][b],
+                                                            acc[a][b], 0, 0, 0);
+      // A wave issues in order and stalls on an MFMA while the matrix unit is
+      // busy, so LDS reads or loads placed after a run of MFMAs would wait for
+      // the whole run.  Ask the scheduler for MFMA, LDS read, load, MFMA, ...
+      // so the memory instructions of the next tap go out under this tap's
+      // matrix work.
+#pragma unroll
+      for (int i = 0; i < FK * FP; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+        __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // one global load (LDS-DMA)
+      }
     }
-    if (more) store_stage(cur ^ 1);
-    __syncthreads();
   }
+  wait_vm_lgkm0<0>();  // no LDS-DMA may outlive the workgroup
 
   // ---- epilogue: int32 -> fp32 -> *alpha -> rint -> clamp -> int8 --------
   // Accumulator layout of v_mfma_i32_32x32x32_i8: lane l, register i holds
@@ -262,30 +429,47 @@ conv_i8_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ w,
 // ---------------------------------------------------------------------------
 // Configuration table.  Each entry is one compiled tile shape.
 // ---------------------------------------------------------------------------
-template <int WK, int WP, int FK, int FP, int KT>
+template <int WK, int WP, int FK, int FP, int KT, int NS, bool RSO>
 static hipError_t launch_i8(const int8_t *x, const int8_t *w, int8_t *y,
                             const I8Params &p, int grid, hipStream_t s) {
-  using T = I8Tile<WK, WP, FK, FP, KT>;
-  hipLaunchKernelGGL((conv_i8_kernel<WK, WP, FK, FP, KT>), dim3(grid),
+  using T = I8Tile<WK, WP, FK, FP, KT, NS>;
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void *>(&conv_i8_kernel<WK, WP, FK, FP, KT, NS, RSO>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS_BYTES);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL((conv_i8_kernel<WK, WP, FK, FP, KT, NS, RSO>), dim3(grid),
                      dim3(T::THREADS), T::LDS_BYTES, s, x, w, y, p);
   return hipGetLastError();
 }
 
-#define I8_CFG(WK, WP, FK, FP, KT)                                              \
+#define I8_CFG(WK, WP, FK, FP, KT, NS, RSO)                                     \
   I8Config {                                                                    \
-    "i8_mfma32x32x32_wg" #WK "x" #WP "_frag" #FK "x" #FP "_kt" #KT "_st2",     \
-        I8Tile<WK, WP, FK, FP, KT>::BM, I8Tile<WK, WP, FK, FP, KT>::BN,         \
-        I8Tile<WK, WP, FK, FP, KT>::THREADS, I8Tile<WK, WP, FK, FP, KT>::LDS_BYTES, \
-        &launch_i8<WK, WP, FK, FP, KT>                                          \
+    "i8_mfma32x32x32_wg" #WK "x" #WP "_frag" #FK "x" #FP "_kt" #KT "_ring" #NS  \
+    "_rsouter_" #RSO,                                                           \
+        I8Tile<WK, WP, FK, FP, KT, NS>::BM, I8Tile<WK, WP, FK, FP, KT, NS>::BN,  \
+        I8Tile<WK, WP, FK, FP, KT, NS>::THREADS,                                \
+        I8Tile<WK, WP, FK, FP, KT, NS>::LDS_BYTES, KT, RSO,                     \
+        &launch_i8<WK, WP, FK, FP, KT, NS, RSO>                                 \
   }
 
 I8Config kI8Configs[] = {
-    I8_CFG(2, 2, 2, 2, 2),  // 0: 128 ch x 128 px, 4 waves of 64x64
-    I8_CFG(1, 4, 2, 1, 4),  // 1: 64 ch x 128 px, 4 waves of 64x32
-    I8_CFG(1, 2, 1, 1, 2),  // 2: 32 ch x 64 px, 2 waves (tiny problems)
-    I8_CFG(2, 2, 2, 4, 2),  // 3: 128 ch x 256 px, 4 waves of 64x128
-    I8_CFG(2, 2, 4, 2, 2),  // 4: 256 ch x 128 px, 4 waves of 128x64
-    I8_CFG(1, 1, 1, 1, 1),  // 5: 32 ch x 32 px, 1 wave
+    // generic tap order (any C/32)
+    I8_CFG(2, 2, 2, 2, 2, 4, false),  // 0: 128 ch x 128 px, 4 waves of 64x64
+    I8_CFG(1, 4, 2, 1, 4, 4, false),  // 1: 64 ch x 128 px, 4 waves of 64x32
+    I8_CFG(1, 2, 1, 1, 2, 4, false),  // 2: 32 ch x 64 px, 2 waves (tiny problems)
+    I8_CFG(1, 1, 1, 1, 2, 4, false),  // 3: 32 ch x 32 px, 1 wave
+    I8_CFG(2, 2, 4, 2, 2, 4, false),  // 4: 256 ch x 128 px, 4 waves of 128x64
+    // (r, s)-outer order (C/32 divisible by the taps per stage)
+    I8_CFG(2, 2, 4, 2, 2, 4, true),   // 5: 256 ch x 128 px, 96 KiB ring
+    I8_CFG(2, 2, 4, 2, 2, 6, true),   // 6: 256 ch x 128 px, 144 KiB ring
+    I8_CFG(2, 2, 4, 2, 4, 3, true),   // 7: 256 ch x 128 px, 4 taps per stage
+    I8_CFG(1, 4, 4, 2, 2, 6, true),   // 8: 128 ch x 256 px, 4 waves of 128x64
+    I8_CFG(2, 2, 2, 2, 2, 4, true),   // 9: 128 ch x 128 px, 64 KiB ring
+    I8_CFG(2, 2, 2, 2, 4, 4, true),   // 10: 128 ch x 128 px, 4 taps per stage
+    I8_CFG(2, 4, 2, 2, 2, 6, true),   // 11: 128 ch x 256 px, 8 waves of 64x64
+    I8_CFG(4, 2, 2, 2, 2, 6, true),   // 12: 256 ch x 128 px, 8 waves of 64x64
+    I8_CFG(2, 4, 2, 2, 4, 3, true),   // 13: 128 ch x 256 px, 8 waves, 4 taps per stage
+    I8_CFG(1, 2, 1, 1, 2, 4, true),   // 14: 32 ch x 64 px, 2 waves
 };
 int kNumI8Configs = sizeof(kI8Configs) / sizeof(kI8Configs[0]);
 

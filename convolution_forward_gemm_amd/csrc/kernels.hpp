@@ -15,7 +15,7 @@ struct I8Params {
   int H, W, HW; // input height, width, plane size
   int CB;       // C/32 input channel blocks
   int K, KBLK;  // output channels and K/32
-  int RS, S;    // filter taps per channel block, filter width
+  int R, S, RS; // filter height, width, taps per channel block
   int ntaps;    // CB*R*S reduction steps of 32 channels
   int ph, pw, sh, sw, dh, dw;
   int k_tiles;  // workgroup tiles along K
@@ -32,6 +32,8 @@ struct I8Config {
   int bn;       // output pixels per workgroup
   int threads;
   int lds_bytes;
+  int kt;        // taps per stage
+  int rs_outer;  // 1: needs (C/32) % kt == 0
   I8LaunchFn launch;
 };
 

@@ -1,0 +1,194 @@
+// peak_probe.hip -- measured throughput ceilings of one MI355X (gfx950),
+// for the roofline of the conv kernels: int8 / fp32 MFMA rate, LDS read
+// bandwidth, L2 -> CU load bandwidth (to VGPRs and LDS-DMA), HBM copy rate.
+// Every kernel touches only its own buffers, at in-bounds offsets.
+// Build: hipcc --offload-arch=gfx950 -O3 peak_probe.hip -o peak_probe
+#include <hip/hip_runtime.h>
+#include <stdio.h>
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+#define LDS __attribute__((address_space(3)))
+
+#define CHECK(x)                                                          \
+  do {                                                                    \
+    hipError_t e_ = (x);                                                  \
+    if (e_ != hipSuccess) {                                               \
+      printf("HIP error %s at line %d\n", hipGetErrorString(e_), __LINE__); \
+      return 1;                                                           \
+    }                                                                     \
+  } while (0)
+
+// Four independent accumulator chains per wave keep the matrix unit busy.
+__global__ void __launch_bounds__(256) mfma_i8(v16i *out, int iters) {
+  int t = threadIdx.x;
+  v4i a = {t, 1, 2, 3}, b = {4, 5, 6, t};
+  v16i c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  for (int i = 0; i < iters; ++i) {
+    c0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c1, 0, 0, 0);
+    c2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c2, 0, 0, 0);
+    c3 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c3, 0, 0, 0);
+  }
+  out[blockIdx.x * 256 + t] = c0 + c1 + c2 + c3;
+}
+
+__global__ void __launch_bounds__(256) mfma_f32(v16f *out, int iters) {
+  float a = threadIdx.x, b = 1.0f;
+  v16f c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  for (int i = 0; i < iters; ++i) {
+    c0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c1, 0, 0, 0);
+    c2 = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c2, 0, 0, 0);
+    c3 = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c3, 0, 0, 0);
+  }
+  out[blockIdx.x * 256 + threadIdx.x] = c0 + c1 + c2 + c3;
+}
+
+// ds_read_b128 with lane-contiguous addresses (the conv kernels' pattern).
+__global__ void __launch_bounds__(256) lds_read(v4i *out, int iters) {
+  __shared__ v4i buf[4096];  // 64 KiB
+  for (int i = threadIdx.x; i < 4096; i += 256) buf[i] = v4i{i, i, i, i};
+  __syncthreads();
+  v4i acc = {};
+  int base = (threadIdx.x >> 6) * 1024 + (threadIdx.x & 63);
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc ^= buf[(base + j * 64 + i * 8) & 4095];
+  }
+  out[blockIdx.x * 256 + threadIdx.x] = acc;
+}
+
+// 1 KiB per wave per load from an L2-resident window, into VGPRs.
+__global__ void __launch_bounds__(256) l2_to_vgpr(const char *src, int win, int iters, v4i *out) {
+  __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)src, (short)0, win, 0x00020000);
+  int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  unsigned off = ((blockIdx.x * 4 + wave) * 8192u + lane * 16u) % (unsigned)win;
+  v4i acc = {};
+  for (int i = 0; i < iters; ++i) {
+    v4i v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      v[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, (off + j * 1024u) % (unsigned)win, 0, 0);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc ^= v[j];
+    off = (off + 8192u) % (unsigned)win;
+  }
+  out[blockIdx.x * 256 + threadIdx.x] = acc;
+}
+
+// The same loads straight into LDS (buffer_load ... lds), 3 stages in flight.
+__global__ void __launch_bounds__(256) l2_to_lds(const char *src, int win, int iters, v4i *out) {
+  __shared__ v4i ring[4][8][64];
+  __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)src, (short)0, win, 0x00020000);
+  int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  unsigned off = ((blockIdx.x * 4 + wave) * 8192u + lane * 16u) % (unsigned)win;
+  v4i acc = {};
+  for (int i = 0; i < iters; ++i) {
+    int st = i & 3;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS void *)&ring[st][wave * 2 + j][0], 16,
+                                               (off + j * 1024u) % (unsigned)win, 0, 0, 0);
+    off = (off + 8192u) % (unsigned)win;
+    __builtin_amdgcn_s_waitcnt((6 & 15) | (7 << 4) | (15 << 8));  // vmcnt(6)
+    acc ^= ring[(i + 1) & 3][wave * 2][lane];
+  }
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+  out[blockIdx.x * 256 + threadIdx.x] = acc;
+}
+
+__global__ void copy_kernel(const v4i *__restrict__ in, v4i *__restrict__ out, size_t n) {
+  size_t i = blockIdx.x * (size_t)256 + threadIdx.x;
+  size_t stride = (size_t)gridDim.x * 256;
+  for (; i < n; i += stride) out[i] = in[i];
+}
+
+int main() {
+  hipDeviceProp_t prop;
+  CHECK(hipGetDeviceProperties(&prop, 0));
+  const int ncu = prop.multiProcessorCount;
+  const double clk = prop.clockRate * 1e3;  // Hz
+  printf("device %s, %d CUs, max clock %.0f MHz\n", prop.gcnArchName, ncu, clk / 1e6);
+  void *out;
+  CHECK(hipMalloc(&out, (size_t)ncu * 8 * 256 * 64 * 4));
+  hipEvent_t e0, e1;
+  CHECK(hipEventCreate(&e0));
+  CHECK(hipEventCreate(&e1));
+  float ms;
+  const int grid = ncu * 2, iters = 20000;
+
+  hipLaunchKernelGGL(mfma_i8, dim3(grid), dim3(256), 0, 0, (v16i *)out, 100);
+  CHECK(hipDeviceSynchronize());
+  CHECK(hipEventRecord(e0));
+  hipLaunchKernelGGL(mfma_i8, dim3(grid), dim3(256), 0, 0, (v16i *)out, iters);
+  CHECK(hipEventRecord(e1));
+  CHECK(hipEventSynchronize(e1));
+  CHECK(hipEventElapsedTime(&ms, e0, e1));
+  printf("int8 MFMA v_mfma_i32_32x32x32_i8 : %8.1f TOPS\n",
+         2.0 * 32 * 32 * 32 * 4 * (double)iters * grid * 4 / ms / 1e9);
+
+  CHECK(hipEventRecord(e0));
+  hipLaunchKernelGGL(mfma_f32, dim3(grid), dim3(256), 0, 0, (v16f *)out, iters / 4);
+  CHECK(hipEventRecord(e1));
+  CHECK(hipEventSynchronize(e1));
+  CHECK(hipEventElapsedTime(&ms, e0, e1));
+  printf("fp32 MFMA v_mfma_f32_32x32x2_f32 : %8.1f TFLOPS\n",
+         2.0 * 32 * 32 * 2 * 4 * (double)(iters / 4) * grid * 4 / ms / 1e9);
+
+  for (int wgs = 1; wgs <= 2; ++wgs) {
+    const int g = ncu * wgs;
+    hipLaunchKernelGGL(lds_read, dim3(g), dim3(256), 0, 0, (v4i *)out, 100);
+    CHECK(hipDeviceSynchronize());
+    CHECK(hipEventRecord(e0));
+    hipLaunchKernelGGL(lds_read, dim3(g), dim3(256), 0, 0, (v4i *)out, iters);
+    CHECK(hipEventRecord(e1));
+    CHECK(hipEventSynchronize(e1));
+    CHECK(hipEventElapsedTime(&ms, e0, e1));
+    const double bytes = 16.0 * 8 * (double)iters * g * 256;
+    printf("LDS ds_read_b128, %d WG/CU          : %8.1f B/clk/CU\n", wgs, bytes / (ms * 1e-3) / ncu / clk);
+  }
+
+  const int win = 2 << 20;  // L2-resident window
+  char *src;
+  CHECK(hipMalloc(&src, win));
+  CHECK(hipMemset(src, 3, win));
+  for (int wgs = 1; wgs <= 2; ++wgs) {
+    const int g = ncu * wgs, it = 4000;
+    hipLaunchKernelGGL(l2_to_vgpr, dim3(g), dim3(256), 0, 0, src, win, 10, (v4i *)out);
+    CHECK(hipDeviceSynchronize());
+    CHECK(hipEventRecord(e0));
+    hipLaunchKernelGGL(l2_to_vgpr, dim3(g), dim3(256), 0, 0, src, win, it, (v4i *)out);
+    CHECK(hipEventRecord(e1));
+    CHECK(hipEventSynchronize(e1));
+    CHECK(hipEventElapsedTime(&ms, e0, e1));
+    double bytes = (double)g * 4 * it * 8192;
+    printf("L2 -> VGPR loads, %d WG/CU         : %8.1f B/clk/CU\n", wgs, bytes / (ms * 1e-3) / ncu / clk);
+    hipLaunchKernelGGL(l2_to_lds, dim3(g), dim3(256), 0, 0, src, win, 10, (v4i *)out);
+    CHECK(hipDeviceSynchronize());
+    CHECK(hipEventRecord(e0));
+    hipLaunchKernelGGL(l2_to_lds, dim3(g), dim3(256), 0, 0, src, win, it, (v4i *)out);
+    CHECK(hipEventRecord(e1));
+    CHECK(hipEventSynchronize(e1));
+    CHECK(hipEventElapsedTime(&ms, e0, e1));
+    bytes = (double)g * 4 * it * 2048;
+    printf("L2 -> LDS (LDS-DMA), %d WG/CU      : %8.1f B/clk/CU\n", wgs, bytes / (ms * 1e-3) / ncu / clk);
+  }
+
+  const size_t n = (size_t)1 << 26;  // 1 GiB of 16-byte elements
+  void *a, *b;
+  CHECK(hipMalloc(&a, n * 16));
+  CHECK(hipMalloc(&b, n * 16));
+  CHECK(hipMemset(a, 1, n * 16));
+  hipLaunchKernelGGL(copy_kernel, dim3(ncu * 16), dim3(256), 0, 0, (const v4i *)a, (v4i *)b, n);
+  CHECK(hipDeviceSynchronize());
+  CHECK(hipEventRecord(e0));
+  for (int r = 0; r < 5; ++r)
+    hipLaunchKernelGGL(copy_kernel, dim3(ncu * 16), dim3(256), 0, 0, (const v4i *)a, (v4i *)b, n);
+  CHECK(hipEventRecord(e1));
+  CHECK(hipEventSynchronize(e1));
+  CHECK(hipEventElapsedTime(&ms, e0, e1));
+  printf("HBM copy 1 GiB (read + write)      : %8.1f GB/s\n", 5 * 2.0 * n * 16 / ms / 1e6);
+  return 0;
+}

@@ -29,6 +29,22 @@ def _b():
     return binding
 
 
+class ConfigNotApplicable(Exception):
+    pass
+
+
+def each_config(dtype, run):
+    """Call run(cfg) for every compiled configuration the problem accepts."""
+    ran = 0
+    for cfg in range(_b().num_configs(dtype)):
+        try:
+            run(cfg)
+        except ConfigNotApplicable:
+            continue
+        ran += 1
+    assert ran >= 1
+
+
 def _dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
@@ -41,7 +57,14 @@ def gpu_conv_i8(x, w, alpha, pad, stride, dil, config=None):
     K, _, R, S = w.shape
     conv = b.Conv2dFprop(N, C, H, W, K, R, S, pad=pad, stride=stride, dil=dil, dtype="int8")
     if config is not None:
-        conv.set_config(config)
+        try:
+            conv.set_config(config)
+        except b.ConvError as e:
+            # e.g. an (r, s)-outer configuration needs C/32 divisible by its
+            # taps per stage
+            if e.status != b.CONV_ERR_UNSUPPORTED:
+                raise
+            raise ConfigNotApplicable(str(e))
     x_il = b.nchw_to_nc32hw32(_dev(x))
     w_il = b.kcrs_to_c32rsk32(_dev(w))
     y = torch.full(conv.y_shape, 77, dtype=torch.int8, device="cuda")  # poison
@@ -118,6 +141,9 @@ RAGGED = [
     (1, 32, 1, 1, 32, 1, 1, (0, 0), (1, 1), (1, 1)),
     (1, 32, 3, 3, 32, 3, 3, (0, 0), (1, 1), (1, 1)),       # single output pixel
     (1, 64, 4, 4, 32, 3, 3, (3, 3), (1, 1), (1, 1)),       # padding wider than kernel reach
+    (2, 256, 9, 7, 320, 3, 3, (1, 1), (1, 1), (1, 1)),     # C/32 = 8, ragged K tile
+    (1, 128, 11, 10, 64, 3, 2, (1, 0), (2, 2), (2, 1)),    # C/32 = 4, stride and dilation
+    (3, 256, 5, 6, 96, 1, 1, (0, 0), (1, 1), (1, 1)),      # 1x1, C/32 = 8
 ]
 
 
@@ -127,10 +153,12 @@ def test_int8_configs_accumulators(case):
     x = wl.int8_uniform((N, C, H, W), -2, 2, 21, *case[:7])
     w = wl.int8_uniform((K, C, R, S), -2, 2, 22, *case[:7])
     acc, ref = oracle_i8_il(x, w, 1.0, pad, stride, dil)
-    for cfg in range(_b().num_configs("int8")):
+
+    def run(cfg):
         _announce("int8 acc", case, "config", cfg)
         y, conv = gpu_conv_i8(x, w, 1.0, pad, stride, dil, config=cfg)
         assert np.array_equal(y, ref), conv.config
+    each_config("int8", run)
 
 
 @pytest.mark.parametrize("case", RAGGED)
@@ -140,10 +168,12 @@ def test_int8_configs_full_range(case):
     w = wl.int8_uniform((K, C, R, S), -128, 127, 24, *case[:7])
     alpha = 2.0 ** -10
     _, ref = oracle_i8_il(x, w, alpha, pad, stride, dil)
-    for cfg in range(_b().num_configs("int8")):
+
+    def run(cfg):
         _announce("int8 full", case, "config", cfg)
         y, conv = gpu_conv_i8(x, w, alpha, pad, stride, dil, config=cfg)
         assert np.array_equal(y, ref), conv.config
+    each_config("int8", run)
 
 
 @pytest.mark.parametrize("seed", range(6))
@@ -221,10 +251,6 @@ def test_run_errors_leave_output_untouched():
 # --------------------------------------------------------------------------
 # fp32
 # --------------------------------------------------------------------------
-class ConfigNotApplicable(Exception):
-    pass
-
-
 def gpu_conv_f32(x, w, pad, stride, dil, alpha=1.0, config=None):
     b = _b()
     N, C, H, W = x.shape
@@ -267,16 +293,12 @@ def test_f32_configs(case):
     N, C, H, W, K, R, S, pad, stride, dil = case
     x, w = wl.make_custom("fp32", N, C, H, W, K, R, S, seed=hash(case) % 1000)
     ref = oracle.conv2d_f32_acc(x, w, pad=pad, stride=stride, dil=dil, nthreads=NTHREADS)
-    ran = 0
-    for cfg in range(_b().num_configs("fp32")):
+
+    def run(cfg):
         _announce("fp32", case, "config", cfg)
-        try:
-            y, conv = gpu_conv_f32(x, w, pad, stride, dil, config=cfg)
-        except ConfigNotApplicable:
-            continue
+        y, conv = gpu_conv_f32(x, w, pad, stride, dil, config=cfg)
         assert_f32_rule(y, ref)
-        ran += 1
-    assert ran >= 1
+    each_config("fp32", run)
 
 
 @pytest.mark.parametrize("case", F32_CASES)
@@ -286,16 +308,12 @@ def test_f32_integer_valued_exact(case):
     x = r.integers(-1, 2, size=(N, C, H, W)).astype(np.float32)
     w = r.integers(-1, 2, size=(K, C, R, S)).astype(np.float32)
     ref = oracle.conv2d_f32_acc(x, w, pad=pad, stride=stride, dil=dil, nthreads=NTHREADS)
-    ran = 0
-    for cfg in range(_b().num_configs("fp32")):
+
+    def run(cfg):
         _announce("fp32 exact", case, "config", cfg)
-        try:
-            y, _ = gpu_conv_f32(x, w, pad, stride, dil, config=cfg)
-        except ConfigNotApplicable:
-            continue
+        y, _ = gpu_conv_f32(x, w, pad, stride, dil, config=cfg)
         assert np.array_equal(y.astype(np.float64), ref)
-        ran += 1
-    assert ran >= 1
+    each_config("fp32", run)
 
 
 def test_f32_workload_c5_sampled():

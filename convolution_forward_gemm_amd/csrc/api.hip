@@ -59,9 +59,11 @@ const ShapeEntry kShapeTable[] = {
     {CONV_DTYPE_INT8, 1, 32, 8, 8, 32, 3, 3, 1, 1, 1, 1, 1, 1, 3},
     // int8 1x1 N2 C128 8x8 K128 (a 128x128x128 GEMM): many small tiles
     {CONV_DTYPE_INT8, 2, 128, 8, 8, 128, 1, 1, 0, 0, 1, 1, 1, 1, 14},
-    // int8 3x3 N32 C256 28x28 K256 and the stride-2 N32 C128 56x56 K256:
-    // 128 ch x 256 px tiles, 8 waves, 4 taps per stage, (r, s)-outer
-    {CONV_DTYPE_INT8, 32, 256, 28, 28, 256, 3, 3, 1, 1, 1, 1, 1, 1, 13},
+    // int8 3x3 N32 C256 28x28 K256: activation halo in LDS, filter
+    // fragments in registers, 128 ch x 256 px tiles, 8 waves of 64x64
+    {CONV_DTYPE_INT8, 32, 256, 28, 28, 256, 3, 3, 1, 1, 1, 1, 1, 1, 20},
+    // int8 3x3 stride-2 N32 C128 56x56 K256: per-tap ring, 128 ch x 256 px
+    // tiles, 8 waves, 4 taps per stage, (r, s)-outer
     {CONV_DTYPE_INT8, 32, 128, 56, 56, 256, 3, 3, 1, 1, 2, 2, 1, 1, 13},
     {CONV_DTYPE_FP32, 8, 32, 512, 512, 64, 5, 9, 2, 4, 1, 1, 2, 3, 0},
 };
@@ -93,13 +95,57 @@ int f32_lds_bytes(const conv2d_fprop_desc_s &d, int cfg) {
   return kF32Configs[cfg].lds_bytes * d.R * d.S;
 }
 
+// int8 configurations: the per-tap ring kernels, then the halo kernels.
+int num_i8_configs() { return kNumI8Configs + kNumI8HaloConfigs; }
+
+const I8Config *i8_config(int cfg) {
+  if (cfg < 0) return nullptr;
+  if (cfg < kNumI8Configs) return &kI8Configs[cfg];
+  if (cfg < num_i8_configs()) return &kI8HaloConfigs[cfg - kNumI8Configs];
+  return nullptr;
+}
+
+// Halo geometry of the LDS-halo kernel for this problem and tile width.
+// Returns false if its LDS or per-wave load budget does not fit.
+bool plan_halo(const conv2d_fprop_desc_s &d, const I8Config &c, int64_t M, I8Params &p) {
+  if (d.R != c.fr || d.S != c.fs) return false;
+  const int64_t HV = (int64_t)d.H + 2 * d.ph;
+  const int64_t WV = (int64_t)(d.Q - 1) * d.sw + (int64_t)(d.S - 1) * d.dw + 1;
+  const int64_t PQ = (int64_t)d.P * d.Q;
+  // Virtual row of the first filter row of output pixel m.
+  auto vrow = [&](int64_t m) { return (m / PQ) * HV + ((m % PQ) / d.Q) * d.sh; };
+  int64_t rows = 0;
+  for (int64_t m0 = 0; m0 < M; m0 += c.bn) {
+    const int64_t m1 = (m0 + c.bn < M ? m0 + c.bn : M) - 1;
+    const int64_t r = vrow(m1) - vrow(m0) + (int64_t)(d.R - 1) * d.dh + 1;
+    if (r > rows) rows = r;
+  }
+  const int64_t dpp = (rows * WV + 63) / 64;  // 1 KiB blocks per half-plane
+  const int64_t hblk = 2 * dpp;
+  if ((hblk + c.nwaves - 1) / c.nwaves > c.hj) return false;
+  // kind 1 stages the filter taps in LDS too; kind 2 keeps them in registers
+  const int64_t filt = c.kind == 1 ? (int64_t)d.R * d.S * (c.bm / 32) * 1024 : 0;
+  const int64_t stage = filt + hblk * 1024;
+  const int64_t lds = c.ns * stage + 1024;
+  if (lds > 160 * 1024) return false;
+  if ((int64_t)d.N * HV > 0x7fffffff) return false;
+  p.HV = (int)HV;
+  p.WV = (int)WV;
+  p.halo_dpp = (int)dpp;
+  p.halo_bytes = (int)(hblk * 1024);
+  p.stage_bytes = (int)stage;
+  p.lds_bytes = (int)lds;
+  return true;
+}
+
 // Fill the launch parameters for configuration `cfg`; false if it cannot run.
 bool plan(conv2d_fprop_desc_s &d, int cfg) {
   const int64_t M = (int64_t)d.N * d.P * d.Q;
   if (d.dtype == CONV_DTYPE_INT8) {
-    if (cfg < 0 || cfg >= kNumI8Configs) return false;
-    const I8Config &c = kI8Configs[cfg];
-    if (c.rs_outer && (d.C / 32) % c.kt != 0) return false;
+    const I8Config *cp = i8_config(cfg);
+    if (!cp) return false;
+    const I8Config &c = *cp;
+    if (c.kind == 0 && c.rs_outer && (d.C / 32) % c.kt != 0) return false;
     const int64_t mt = (M + c.bn - 1) / c.bn, kt = (d.K + c.bm - 1) / c.bm;
     if (mt * kt > 0x7fffffff) return false;
     I8Params &p = d.i8;
@@ -121,6 +167,10 @@ bool plan(conv2d_fprop_desc_s &d, int cfg) {
     p.x_bytes = (uint32_t)d.x_bytes;
     p.w_bytes = (uint32_t)d.w_bytes;
     p.alpha = 1.0f;
+    p.N = d.N;
+    p.HV = p.WV = p.halo_dpp = p.halo_bytes = p.stage_bytes = 0;
+    p.lds_bytes = c.lds_bytes;
+    if (c.kind != 0 && !plan_halo(d, c, M, p)) return false;
     d.grid = (int)(mt * kt);
   } else {
     if (cfg < 0 || cfg >= kNumF32Configs) return false;
@@ -215,7 +265,7 @@ conv_status_t conv2d_fprop_desc_create(conv2d_fprop_desc_t *out, int N, int C,
   if (cfg < 0) cfg = dtype == CONV_DTYPE_INT8 ? heuristic_i8(*d) : heuristic_f32(*d);
   bool ok = plan(*d, cfg);
   if (!ok) {  // try every compiled configuration before giving up
-    const int n = dtype == CONV_DTYPE_INT8 ? kNumI8Configs : kNumF32Configs;
+    const int n = dtype == CONV_DTYPE_INT8 ? num_i8_configs() : kNumF32Configs;
     for (int c = 0; c < n && !ok; ++c) ok = plan(*d, c);
   }
   if (!ok) {
@@ -242,16 +292,16 @@ conv_status_t conv2d_fprop_desc_get_config(conv2d_fprop_desc_t d, char *buf, siz
   if (!d || !buf) return CONV_ERR_NULL;
   if (n == 0) return CONV_OK;
   const bool i8 = d->dtype == CONV_DTYPE_INT8;
-  const char *name = i8 ? kI8Configs[d->config].name : kF32Configs[d->config].name;
-  const int bm = i8 ? kI8Configs[d->config].bm : kF32Configs[d->config].bm;
-  const int bn = i8 ? kI8Configs[d->config].bn : kF32Configs[d->config].bn;
+  const char *name = i8 ? i8_config(d->config)->name : kF32Configs[d->config].name;
+  const int bm = i8 ? i8_config(d->config)->bm : kF32Configs[d->config].bm;
+  const int bn = i8 ? i8_config(d->config)->bn : kF32Configs[d->config].bn;
   snprintf(buf, n, "config=%d %s tile=%dch x %dpx grid=%d", d->config, name, bm, bn,
            d->grid);
   return CONV_OK;
 }
 
 int conv2d_fprop_num_configs(conv_dtype_t dtype) {
-  if (dtype == CONV_DTYPE_INT8) return kNumI8Configs;
+  if (dtype == CONV_DTYPE_INT8) return num_i8_configs();
   if (dtype == CONV_DTYPE_FP32) return kNumF32Configs;
   return 0;
 }
@@ -276,7 +326,7 @@ conv_status_t conv2d_fprop_run(conv2d_fprop_desc_t d, const void *x, const void 
   if (d->dtype == CONV_DTYPE_INT8) {
     I8Params p = d->i8;
     p.alpha = alpha;
-    e = kI8Configs[d->config].launch((const int8_t *)x, (const int8_t *)w, (int8_t *)y, p,
+    e = i8_config(d->config)->launch((const int8_t *)x, (const int8_t *)w, (int8_t *)y, p,
                                      d->grid, stream);
   } else {
     F32Params p = d->f32;

@@ -34,8 +34,22 @@ __device__ __forceinline__ v4i load_b128(__amdgpu_buffer_rsrc_t r, uint32_t off)
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
 
+// 16-byte load with a wave-uniform soffset added to the per-lane offset.
+__device__ __forceinline__ v4i load_b128_s(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, __builtin_amdgcn_readfirstlane(soff), 0);
+}
+
 __device__ __forceinline__ float load_f32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
+// One LDS-DMA load: 64 lanes x 16 bytes from the buffer into LDS at dst +
+// 16*lane (dst wave-uniform).  The per-lane offset is voff, a wave-uniform
+// offset soff is added to it; an out-of-range voff writes zeros.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, unsigned char *dst,
+                                          uint32_t voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)dst, 16,
+                                           voff, __builtin_amdgcn_readfirstlane(soff), 0, 0);
 }
 
 // Launch-grid remap that keeps neighbouring logical tiles on one XCD.

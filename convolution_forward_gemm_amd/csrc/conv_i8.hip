@@ -34,6 +34,7 @@
 //   * The epilogue converts, scales, rounds half-to-even and saturates in
 //     registers, then writes four channels per 32-bit store.
 #include "common.hpp"
+#include "epilogue_i8.hpp"
 #include "kernels.hpp"
 
 namespace convfprop {
@@ -228,12 +229,10 @@ conv_i8_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ w,
   // Padded taps, pixels past M and channels past K use OOB_OFFSET as voffset
   // and the buffer unit writes zeros.  The range check sees voffset only, so
   // every in-range access must have a non-negative voffset of its own.
-  // soff is wave-uniform by construction; readfirstlane states it so that the
-  // compiler keeps it in an SGPR instead of wrapping the load in a loop.
+  // soff is wave-uniform by construction (lds_dma16 states so to the
+  // compiler, which then keeps it in an SGPR).
   auto dma = [&](__amdgpu_buffer_rsrc_t r, unsigned char *dst, uint32_t voff, int soff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        r, (__attribute__((address_space(3))) void *)dst, 16, voff,
-        __builtin_amdgcn_readfirstlane(soff), 0, 0);
+    lds_dma16(r, dst, voff, soff);
   };
 
   // (cb, r, s) walker state for the generic order.
@@ -393,37 +392,7 @@ conv_i8_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ w,
   }
   wait_vm_lgkm0<0>();  // no LDS-DMA may outlive the workgroup
 
-  // ---- epilogue: int32 -> fp32 -> *alpha -> rint -> clamp -> int8 --------
-  // Accumulator layout of v_mfma_i32_32x32x32_i8: lane l, register i holds
-  // D[row = 8*(i/4) + 4*(l/32) + i%4][col = l%32].  Rows are channels, so the
-  // quad i = 4g..4g+3 is channels 8g + 4*(l/32) + 0..3 of pixel l%32.
-  const float alpha = p.alpha;
-#pragma unroll
-  for (int b = 0; b < FP; ++b) {
-    const int m = m0 + 32 * (wp * FP + b) + l32;
-    if (m >= p.M) continue;
-    const int n = m / p.PQ;
-    const int pq = m - n * p.PQ;
-#pragma unroll
-    for (int a = 0; a < FK; ++a) {
-      const int kb = k0 / 32 + wk * FK + a;
-      if (kb >= p.KBLK) continue;
-      int8_t *dst = y + ((size_t)(n * p.KBLK + kb) * p.PQ + pq) * 32 + 4 * half;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        uint32_t packed = 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float f = (float)acc[a][b][4 * g + e];
-          f = f * alpha;
-          f = __builtin_rintf(f);
-          f = __builtin_fminf(__builtin_fmaxf(f, -128.0f), 127.0f);
-          packed |= ((uint32_t)(int)f & 0xffu) << (8 * e);
-        }
-        *reinterpret_cast<uint32_t *>(dst + 8 * g) = packed;
-      }
-    }
-  }
+  store_i8_tile<FK, FP>(acc, y, p, m0 + 32 * wp * FP, k0 / 32 + wk * FK, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -449,7 +418,7 @@ static hipError_t launch_i8(const int8_t *x, const int8_t *w, int8_t *y,
         I8Tile<WK, WP, FK, FP, KT, NS>::BM, I8Tile<WK, WP, FK, FP, KT, NS>::BN,  \
         I8Tile<WK, WP, FK, FP, KT, NS>::THREADS,                                \
         I8Tile<WK, WP, FK, FP, KT, NS>::LDS_BYTES, KT, RSO,                     \
-        &launch_i8<WK, WP, FK, FP, KT, NS, RSO>                                 \
+        &launch_i8<WK, WP, FK, FP, KT, NS, RSO>, 0, 0, 0, WK * WP, NS, 0        \
   }
 
 I8Config kI8Configs[] = {

@@ -1,0 +1,518 @@
+// conv_i8_halo.hip -- int8 implicit-GEMM conv2d fprop for gfx950 with an
+// LDS-resident activation halo (filter size fixed at compile time).
+//
+// What is computed is the same as conv_i8.hip (CUTLASS issue 2996, "How to
+// optimize cutlass int8 fprop2d kernel with NCxHWx interleaved layout",
+// section "CUTLASS Kernel Configuration"): int8 products, int32 sums over
+// C*R*S, the alpha / rint / saturate epilogue, NCxHWx<32> / CxRSKx<32>.
+//
+// How it differs from the per-tap ring of conv_i8.hip: a stage is one
+// 32-channel block.  It holds the R*S filter taps of the workgroup's output
+// channels and, once, the input halo those channels' output pixels read:
+// every input row and column any of the R*S taps touches.  All R*S taps then
+// read their pixel fragments from that one halo with per-lane LDS addresses,
+// instead of each tap bringing its own copy from L2.  For a 3x3 filter this
+// cuts the bytes a workgroup pulls from L2 per tap by about half and the
+// activation load instructions several-fold; the L2 -> CU path, not the
+// matrix unit, is what bounds the per-tap design.  (The filter-size
+// specialisation mirrors the "t1r3s3" in the TensorRT kernel name quoted in
+// the same issue, section "TensorRT Kernel Name".)
+//
+// Halo geometry.  Rows are "virtual": image n owns rows n*HV .. n*HV+HV-1
+// with HV = H + 2*pad_h, the first and last pad_h of them being zero
+// padding.  Output pixel (n, p, q) with filter tap (r, s) reads virtual row
+// n*HV + p*sh + r*dh and column q*sw + s*dw (column c is input column
+// c - pad_w).  A workgroup's pixels, even across an image boundary, thus read
+// one contiguous range of virtual rows starting at V_lo (its first pixel's
+// row); the rows and columns outside the image are loaded as zeros.  The
+// halo is stored as two half-planes, bytes 0..15 and 16..31 of each 32-channel
+// vector, each [row][col][16 B]: a fragment read is 32 consecutive 16-byte
+// slots per half-wave, conflict-free.
+#include <type_traits>
+
+#include "common.hpp"
+#include "epilogue_i8.hpp"
+#include "kernels.hpp"
+
+namespace convfprop {
+
+template <int WK, int WP, int FK, int FP, int R, int S, int NS, int HJ>
+struct HaloTile {
+  static constexpr int NWAVES = WK * WP;
+  static constexpr int THREADS = 64 * NWAVES;
+  static constexpr int KB = WK * FK;
+  static constexpr int PB = WP * FP;
+  static constexpr int BM = 32 * KB;
+  static constexpr int BN = 32 * PB;
+  static constexpr int RS = R * S;
+  static constexpr int FBLK = RS * KB;                          // filter blocks per stage
+  static constexpr int FJ = (FBLK + NWAVES - 1) / NWAVES;       // filter DMAs per wave
+  static constexpr int NL = FJ + HJ;                            // DMAs per wave per stage
+  static constexpr int FILT_BYTES = FBLK * 1024;
+  static_assert(NS >= 3, "the ring needs a stage being read, one landed and one in flight");
+  static_assert(NL * (NS - 2) < 64, "vmcnt counts at most 63 outstanding loads");
+};
+
+// s_waitcnt vmcnt(VM) lgkmcnt(0) (gfx9 encoding), and a barrier without the
+// fence of __syncthreads (which would drain every LDS-DMA in flight).
+template <int VM>
+__device__ __forceinline__ void halo_wait() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | ((VM >> 4) << 14));
+}
+__device__ __forceinline__ void halo_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int WK, int WP, int FK, int FP, int R, int S, int NS, int HJ>
+__global__ void __launch_bounds__(64 * WK * WP)
+conv_i8_halo_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ w,
+                    int8_t *__restrict__ y, I8Params p) {
+  using T = HaloTile<WK, WP, FK, FP, R, S, NS, HJ>;
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+
+  const int tile = xcd_remap(blockIdx.x, gridDim.x);
+  const int ktile = tile % p.k_tiles;
+  const int mtile = tile / p.k_tiles;
+  const int k0 = ktile * T::BM;
+  const int m0 = mtile * T::BN;
+
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, p.x_bytes);
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(w, p.w_bytes);
+
+  const int HV = p.HV, WV = p.WV;
+  const int plane = p.halo_dpp * 1024;  // bytes per half-plane
+  const int hblk = 2 * p.halo_dpp;      // halo DMA blocks per stage
+  unsigned char *dummy = lds + NS * p.stage_bytes;  // 1 KiB sink for padding DMAs
+
+  // First virtual row of the workgroup's halo (wave-uniform).
+  const int n_first = m0 / p.PQ;
+  const int p_first = (m0 - n_first * p.PQ) / p.Q;
+  const int v_lo = n_first * HV + p_first * p.sh;
+
+  // ---- per-lane halo DMA sources (channel block 0), fixed for all stages --
+  uint32_t hv_off[HJ];
+  int hv_dst[HJ];  // LDS offset within the halo, or -1 for the sink
+#pragma unroll
+  for (int j = 0; j < HJ; ++j) {
+    const int g = j * T::NWAVES + wave;  // this wave's j-th halo block
+    uint32_t off = OOB_OFFSET;
+    int dst = -1;
+    if (g < hblk) {
+      const int hp = g >= p.halo_dpp;               // half-plane
+      const int slot = (g - hp * p.halo_dpp) * 64 + lane;
+      const int row = slot / WV;
+      const int col = slot - row * WV;
+      const int v = v_lo + row;
+      const int n = v / HV;
+      const int ih = v - n * HV - p.ph;
+      const int iw = col - p.pw;
+      if (n < p.N && (unsigned)ih < (unsigned)p.H && (unsigned)iw < (unsigned)p.W)
+        off = (uint32_t)(((n * p.CB * p.H + ih) * p.W + iw) * 32 + hp * 16);
+      dst = hp * plane + (g - hp * p.halo_dpp) * 1024;
+    }
+    hv_off[j] = off;
+    hv_dst[j] = dst;
+  }
+
+  // ---- per-lane filter DMA sources: block g = (tap, kb) ------------------
+  uint32_t fv_off[T::FJ];
+#pragma unroll
+  for (int j = 0; j < T::FJ; ++j) {
+    const int g = j * T::NWAVES + wave;
+    const int kb = g % T::KB;
+    const int k = k0 + 32 * kb + l32;
+    fv_off[j] = (g < T::FBLK && k < p.K) ? (uint32_t)(k * 32 + 16 * half) : OOB_OFFSET;
+  }
+
+  // ---- per-lane pixel fragment addresses inside the halo -----------------
+  const int wk = wave % WK;
+  const int wp = wave / WK;
+  int b_addr[FP];
+#pragma unroll
+  for (int i = 0; i < FP; ++i) {
+    const int m = m0 + 32 * (wp * FP + i) + l32;
+    int a = 0;  // pixels past M read any valid slot; their columns are not stored
+    if (m < p.M) {
+      const int n = m / p.PQ;
+      const int pq = m - n * p.PQ;
+      const int op = pq / p.Q;
+      const int oq = pq - op * p.Q;
+      a = ((n * HV + op * p.sh - v_lo) * WV + oq * p.sw) * 16;
+    }
+    b_addr[i] = T::FILT_BYTES + half * plane + a;
+  }
+  // LDS offset of tap t = (r, s) relative to the pixel's tap (0, 0).
+  int tap_off[T::RS];
+#pragma unroll
+  for (int t = 0; t < T::RS; ++t) tap_off[t] = ((t / S) * p.dh * WV + (t % S) * p.dw) * 16;
+
+  const int CB = p.CB;
+  const int HW32 = p.HW * 32;
+  const int KB32 = p.K * 32;
+
+  // Issue the DMAs of channel block `st` into ring slot st % NS.  Blocks
+  // past the reduction are issued with every lane out of range (they zero a
+  // consumed slot) so that every wave always has exactly NL loads per stage.
+  auto issue_stage = [&](int st) {
+    unsigned char *base = lds + (st % NS) * p.stage_bytes;
+    const bool live = st < CB;
+#pragma unroll
+    for (int j = 0; j < HJ; ++j) {
+      unsigned char *dst = hv_dst[j] >= 0 ? base + T::FILT_BYTES + hv_dst[j] : dummy;
+      lds_dma16(xr, dst, live ? hv_off[j] : OOB_OFFSET, live ? st * HW32 : 0);
+    }
+#pragma unroll
+    for (int j = 0; j < T::FJ; ++j) {
+      const int g = j * T::NWAVES + wave;
+      const int tap = g / T::KB;
+      const int kb = g - tap * T::KB;
+      unsigned char *dst = g < T::FBLK ? base + (tap * T::KB + kb) * 1024 : dummy;
+      lds_dma16(wr, dst, live ? fv_off[j] : OOB_OFFSET,
+                live && g < T::FBLK ? (st * T::RS + tap) * KB32 : 0);
+    }
+  };
+
+  v4i af[2][FK], bf[2][FP];
+  auto read_frags = [&](int st, int t, v4i (&a)[FK], v4i (&b)[FP]) {
+    const unsigned char *base = lds + (st % NS) * p.stage_bytes;
+#pragma unroll
+    for (int i = 0; i < FK; ++i)
+      a[i] = *reinterpret_cast<const v4i *>(base + ((t * T::KB + wk * FK + i) * 64 + lane) * 16);
+#pragma unroll
+    for (int i = 0; i < FP; ++i)
+      b[i] = *reinterpret_cast<const v4i *>(base + b_addr[i] + tap_off[t]);
+  };
+
+  v16i acc[FK][FP];
+#pragma unroll
+  for (int a = 0; a < FK; ++a)
+#pragma unroll
+    for (int b = 0; b < FP; ++b) acc[a][b] = v16i{0};
+
+  // Ring schedule as in conv_i8.hip: barrier B_k certifies stage k landed and
+  // stage k-2 fully read; B_{st+1} sits before the last tap of stage st.
+#pragma unroll
+  for (int s0 = 0; s0 < NS - 1; ++s0) issue_stage(s0);
+  halo_wait<T::NL * (NS - 2)>();
+  halo_barrier();
+  read_frags(0, 0, af[0], bf[0]);
+
+  // One stage; PAR is the fragment buffer of its tap 0 (R*S may be odd).
+  auto stage = [&](auto par_c, int st) {
+    constexpr int PAR = decltype(par_c)::value;
+#pragma unroll
+    for (int t = 0; t < T::RS; ++t) {
+      const int cur = (t + PAR) & 1;
+      const int nxt = (t + 1 + PAR) & 1;
+      if (t + 1 < T::RS) {
+        read_frags(st, t + 1, af[nxt], bf[nxt]);
+      } else {
+        halo_wait<T::NL * (NS - 3)>();
+        halo_barrier();
+        issue_stage(st + NS - 1);
+        read_frags(st + 1, 0, af[nxt], bf[nxt]);
+      }
+#pragma unroll
+      for (int a = 0; a < FK; ++a)
+#pragma unroll
+        for (int b = 0; b < FP; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[cur][a], bf[cur][b], acc[a][b], 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < FK * FP; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+        __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // one LDS-DMA load
+      }
+    }
+  };
+  using Par0 = std::integral_constant<int, 0>;
+  using Par1 = std::integral_constant<int, 1>;
+  if constexpr (T::RS % 2 == 0) {
+    for (int st = 0; st < CB; ++st) stage(Par0{}, st);
+  } else {
+    for (int st = 0; st < CB; st += 2) {
+      stage(Par0{}, st);
+      if (st + 1 < CB) stage(Par1{}, st + 1);
+    }
+  }
+  halo_wait<0>();  // no LDS-DMA may outlive the workgroup
+
+  store_i8_tile<FK, FP>(acc, y, p, m0 + 32 * wp * FP, k0 / 32 + wk * FK, lane);
+}
+
+// ---------------------------------------------------------------------------
+// Variant with the filter operand in registers.  Each wave loads its own
+// MFMA filter fragments straight from global memory (16 bytes per lane, the
+// MFMA operand order of CxRSKx<32>), RS-1 taps ahead, into a ring of RS
+// register slots; LDS holds only the activation halo.  This halves the LDS
+// bytes read per MFMA -- with 64-wide fragments LDS reads, not the matrix
+// unit, bound the all-LDS variant -- and shrinks a stage to the halo alone.
+//
+// Wait accounting: the halo LDS-DMAs and the filter loads share vmcnt, which
+// retires in issue order.  sched_barrier pins the order of the two streams,
+// so the number of loads issued after a stage's halo batch is known:
+//   prologue:  (NS-2)*HJ + AHEAD*FK
+//   boundary:  (NS-3)*HJ + min((NS-2)*RS, AHEAD+RS)*FK   (a lower bound that
+//              also holds in the first stages, fed by the prologue)
+template <int WK, int WP, int FK, int FP, int R, int S, int NS, int HJ>
+struct HaloAdTile {
+  static constexpr int NWAVES = WK * WP;
+  static constexpr int THREADS = 64 * NWAVES;
+  static constexpr int KB = WK * FK;
+  static constexpr int PB = WP * FP;
+  static constexpr int BM = 32 * KB;
+  static constexpr int BN = 32 * PB;
+  static constexpr int RS = R * S;
+  static constexpr int AHEAD = RS - 1;
+  static constexpr int WAIT0 = (NS - 2) * HJ + AHEAD * FK;
+  static constexpr int WAITL =
+      (NS - 3) * HJ + ((NS - 2) * RS < AHEAD + RS ? (NS - 2) * RS : AHEAD + RS) * FK;
+  static_assert(NS >= 3, "the ring needs a stage being read, one landed and one in flight");
+  static_assert(WAIT0 < 64 && WAITL < 64, "vmcnt counts at most 63 outstanding loads");
+};
+
+template <int WK, int WP, int FK, int FP, int R, int S, int NS, int HJ>
+__global__ void __launch_bounds__(64 * WK * WP)
+conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ w,
+                       int8_t *__restrict__ y, I8Params p) {
+  using T = HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ>;
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+
+  const int tile = xcd_remap(blockIdx.x, gridDim.x);
+  const int ktile = tile % p.k_tiles;
+  const int mtile = tile / p.k_tiles;
+  const int k0 = ktile * T::BM;
+  const int m0 = mtile * T::BN;
+
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, p.x_bytes);
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(w, p.w_bytes);
+
+  const int HV = p.HV, WV = p.WV;
+  const int plane = p.halo_dpp * 1024;
+  const int hblk = 2 * p.halo_dpp;
+  unsigned char *dummy = lds + NS * p.stage_bytes;
+
+  const int n_first = m0 / p.PQ;
+  const int p_first = (m0 - n_first * p.PQ) / p.Q;
+  const int v_lo = n_first * HV + p_first * p.sh;
+
+  // ---- per-lane halo DMA sources (channel block 0) ------------------------
+  uint32_t hv_off[HJ];
+  int hv_dst[HJ];
+#pragma unroll
+  for (int j = 0; j < HJ; ++j) {
+    const int g = j * T::NWAVES + wave;
+    uint32_t off = OOB_OFFSET;
+    int dst = -1;
+    if (g < hblk) {
+      const int hp = g >= p.halo_dpp;
+      const int slot = (g - hp * p.halo_dpp) * 64 + lane;
+      const int row = slot / WV;
+      const int col = slot - row * WV;
+      const int v = v_lo + row;
+      const int n = v / HV;
+      const int ih = v - n * HV - p.ph;
+      const int iw = col - p.pw;
+      if (n < p.N && (unsigned)ih < (unsigned)p.H && (unsigned)iw < (unsigned)p.W)
+        off = (uint32_t)(((n * p.CB * p.H + ih) * p.W + iw) * 32 + hp * 16);
+      dst = hp * plane + (g - hp * p.halo_dpp) * 1024;
+    }
+    hv_off[j] = off;
+    hv_dst[j] = dst;
+  }
+
+  const int wk = wave % WK;
+  const int wp = wave / WK;
+
+  // ---- per-lane filter fragment offsets (channels past K read zeros) ------
+  uint32_t a_off[FK];
+#pragma unroll
+  for (int i = 0; i < FK; ++i) {
+    const int k = k0 + 32 * (wk * FK + i) + l32;
+    a_off[i] = k < p.K ? (uint32_t)(k * 32 + 16 * half) : OOB_OFFSET;
+  }
+
+  // ---- per-lane pixel fragment addresses inside the halo -----------------
+  int b_addr[FP];
+#pragma unroll
+  for (int i = 0; i < FP; ++i) {
+    const int m = m0 + 32 * (wp * FP + i) + l32;
+    int a = 0;
+    if (m < p.M) {
+      const int n = m / p.PQ;
+      const int pq = m - n * p.PQ;
+      const int op = pq / p.Q;
+      const int oq = pq - op * p.Q;
+      a = ((n * HV + op * p.sh - v_lo) * WV + oq * p.sw) * 16;
+    }
+    b_addr[i] = half * plane + a;
+  }
+  int tap_off[T::RS];
+#pragma unroll
+  for (int t = 0; t < T::RS; ++t) tap_off[t] = ((t / S) * p.dh * WV + (t % S) * p.dw) * 16;
+
+  const int CB = p.CB;
+  const int ntaps = CB * T::RS;
+  const int HW32 = p.HW * 32;
+  const int KB32 = p.K * 32;
+
+  auto issue_stage = [&](int st) {
+    unsigned char *base = lds + (st % NS) * p.stage_bytes;
+    const bool live = st < CB;
+#pragma unroll
+    for (int j = 0; j < HJ; ++j) {
+      unsigned char *dst = hv_dst[j] >= 0 ? base + hv_dst[j] : dummy;
+      lds_dma16(xr, dst, live ? hv_off[j] : OOB_OFFSET, live ? st * HW32 : 0);
+    }
+  };
+
+  // Filter fragments of global tap g = cb*RS + t into a register slot.
+  v4i aring[T::RS][FK];
+  auto load_a = [&](int g, v4i (&dst)[FK]) {
+    const bool live = g < ntaps;
+#pragma unroll
+    for (int i = 0; i < FK; ++i)
+      dst[i] = load_b128_s(wr, live ? a_off[i] : OOB_OFFSET, live ? g * KB32 : 0);
+  };
+
+  v4i bf[2][FP];
+  auto read_b = [&](int st, int t, v4i (&b)[FP]) {
+    const unsigned char *base = lds + (st % NS) * p.stage_bytes;
+#pragma unroll
+    for (int i = 0; i < FP; ++i)
+      b[i] = *reinterpret_cast<const v4i *>(base + b_addr[i] + tap_off[t]);
+  };
+
+  v16i acc[FK][FP];
+#pragma unroll
+  for (int a = 0; a < FK; ++a)
+#pragma unroll
+    for (int b = 0; b < FP; ++b) acc[a][b] = v16i{0};
+
+#pragma unroll
+  for (int s0 = 0; s0 < NS - 1; ++s0) issue_stage(s0);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int g = 0; g < T::AHEAD; ++g) load_a(g, aring[g]);
+  __builtin_amdgcn_sched_barrier(0);
+  halo_wait<T::WAIT0>();
+  halo_barrier();
+  read_b(0, 0, bf[0]);
+
+  auto stage = [&](auto par_c, int st) {
+    constexpr int PAR = decltype(par_c)::value;
+#pragma unroll
+    for (int t = 0; t < T::RS; ++t) {
+      const int cur = (t + PAR) & 1;
+      const int nxt = (t + 1 + PAR) & 1;
+      load_a(st * T::RS + t + T::AHEAD, aring[(t + T::AHEAD) % T::RS]);
+      if (t + 1 < T::RS) {
+        read_b(st, t + 1, bf[nxt]);
+      } else {
+        __builtin_amdgcn_sched_barrier(0);
+        halo_wait<T::WAITL>();
+        halo_barrier();
+        issue_stage(st + NS - 1);
+        __builtin_amdgcn_sched_barrier(0);
+        read_b(st + 1, 0, bf[nxt]);
+      }
+#pragma unroll
+      for (int a = 0; a < FK; ++a)
+#pragma unroll
+        for (int b = 0; b < FP; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(aring[t][a], bf[cur][b], acc[a][b], 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < FK * FP; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one filter load
+      }
+    }
+  };
+  using Par0 = std::integral_constant<int, 0>;
+  using Par1 = std::integral_constant<int, 1>;
+  if constexpr (T::RS % 2 == 0) {
+    for (int st = 0; st < CB; ++st) stage(Par0{}, st);
+  } else {
+    for (int st = 0; st < CB; st += 2) {
+      stage(Par0{}, st);
+      if (st + 1 < CB) stage(Par1{}, st + 1);
+    }
+  }
+  halo_wait<0>();
+
+  store_i8_tile<FK, FP>(acc, y, p, m0 + 32 * wp * FP, k0 / 32 + wk * FK, lane);
+}
+
+template <int WK, int WP, int FK, int FP, int R, int S, int NS, int HJ>
+static hipError_t launch_i8_halo_ad(const int8_t *x, const int8_t *w, int8_t *y,
+                                    const I8Params &p, int grid, hipStream_t s) {
+  using T = HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ>;
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void *>(&conv_i8_halo_ad_kernel<WK, WP, FK, FP, R, S, NS, HJ>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL((conv_i8_halo_ad_kernel<WK, WP, FK, FP, R, S, NS, HJ>), dim3(grid),
+                     dim3(T::THREADS), p.lds_bytes, s, x, w, y, p);
+  return hipGetLastError();
+}
+
+template <int WK, int WP, int FK, int FP, int R, int S, int NS, int HJ>
+static hipError_t launch_i8_halo(const int8_t *x, const int8_t *w, int8_t *y,
+                                 const I8Params &p, int grid, hipStream_t s) {
+  using T = HaloTile<WK, WP, FK, FP, R, S, NS, HJ>;
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void *>(&conv_i8_halo_kernel<WK, WP, FK, FP, R, S, NS, HJ>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL((conv_i8_halo_kernel<WK, WP, FK, FP, R, S, NS, HJ>), dim3(grid),
+                     dim3(T::THREADS), p.lds_bytes, s, x, w, y, p);
+  return hipGetLastError();
+}
+
+#define I8_HALO_CFG(WK, WP, FK, FP, R, S, NS, HJ)                                     \
+  I8Config {                                                                          \
+    "i8_halo_mfma32x32x32_wg" #WK "x" #WP "_frag" #FK "x" #FP "_r" #R "s" #S "_ring" #NS, \
+        HaloTile<WK, WP, FK, FP, R, S, NS, HJ>::BM, HaloTile<WK, WP, FK, FP, R, S, NS, HJ>::BN, \
+        HaloTile<WK, WP, FK, FP, R, S, NS, HJ>::THREADS, 0, R * S, 0,                  \
+        &launch_i8_halo<WK, WP, FK, FP, R, S, NS, HJ>, 1, R, S, WK * WP, NS, HJ        \
+  }
+
+#define I8_HALO_AD_CFG(WK, WP, FK, FP, R, S, NS, HJ)                                  \
+  I8Config {                                                                          \
+    "i8_halo_regfilter_mfma32x32x32_wg" #WK "x" #WP "_frag" #FK "x" #FP "_r" #R "s" #S "_ring" #NS, \
+        HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ>::BM, HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ>::BN, \
+        HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ>::THREADS, 0, R * S, 0,                \
+        &launch_i8_halo_ad<WK, WP, FK, FP, R, S, NS, HJ>, 2, R, S, WK * WP, NS, HJ     \
+  }
+
+I8Config kI8HaloConfigs[] = {
+    I8_HALO_CFG(2, 4, 2, 2, 3, 3, 3, 4),  // 128 ch x 256 px, 8 waves of 64x64
+    I8_HALO_CFG(1, 4, 4, 2, 3, 3, 3, 6),  // 128 ch x 256 px, 4 waves of 128x64
+    I8_HALO_CFG(2, 2, 2, 2, 3, 3, 3, 6),  // 128 ch x 128 px, 4 waves of 64x64
+    I8_HALO_CFG(1, 4, 2, 2, 3, 3, 3, 6),  // 64 ch x 256 px, 4 waves of 64x64
+    // filter fragments in registers, LDS holds the halo only
+    I8_HALO_AD_CFG(2, 2, 2, 4, 3, 3, 4, 8),  // 128 ch x 256 px, 4 waves of 64x128
+    I8_HALO_AD_CFG(2, 4, 2, 2, 3, 3, 4, 4),  // 128 ch x 256 px, 8 waves of 64x64
+    I8_HALO_AD_CFG(2, 2, 2, 4, 3, 3, 3, 16), // 128 ch x 256 px, 4 waves, large halos
+    I8_HALO_AD_CFG(2, 2, 2, 2, 3, 3, 4, 8),  // 128 ch x 128 px, 4 waves of 64x64
+    I8_HALO_AD_CFG(2, 4, 2, 2, 3, 3, 3, 8),  // 128 ch x 256 px, 8 waves, large halos
+};
+int kNumI8HaloConfigs = sizeof(kI8HaloConfigs) / sizeof(kI8HaloConfigs[0]);
+
+}  // namespace convfprop

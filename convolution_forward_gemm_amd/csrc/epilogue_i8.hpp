@@ -1,0 +1,60 @@
+// epilogue_i8.hpp -- the fused int8 epilogue shared by the int8 kernels.
+//
+// CUTLASS issue 2996 ("How to optimize cutlass int8 fprop2d kernel with
+// NCxHWx interleaved layout"), section "CUTLASS Kernel Configuration": the
+// int32 accumulator is scaled by an fp32 alpha only and clamped to int8
+// (LinearCombinationClamp, OnlyAlphaScaling).  Order, one rounding per step:
+//   f = fl32(acc)  (round to nearest even)
+//   g = f * alpha  (one fp32 multiply; the build forbids FMA contraction)
+//   r = rint(g)    (round half to even)
+//   y = clamp(r, -128, 127)
+#pragma once
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace convfprop {
+
+// Stores an FK x FP grid of 32x32 MFMA accumulator tiles (rows = output
+// channels, columns = output pixels) into y in NCxHWx<32> over K.
+// Accumulator layout of v_mfma_i32_32x32x32_i8: lane l, register i holds
+// D[row = 8*(i/4) + 4*(l/32) + i%4][col = l%32], so the quad i = 4g..4g+3 is
+// channels 8g + 4*(l/32) + 0..3 of pixel l%32: one packed 32-bit store.
+//   m_base: first pixel of fragment column 0; kb_base: first 32-channel
+//   block of fragment row 0.  Pixels past M and blocks past K/32 are skipped.
+template <int FK, int FP>
+__device__ __forceinline__ void store_i8_tile(const v16i (&acc)[FK][FP], int8_t *__restrict__ y,
+                                              const I8Params &p, int m_base, int kb_base,
+                                              int lane) {
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+  const float alpha = p.alpha;
+#pragma unroll
+  for (int b = 0; b < FP; ++b) {
+    const int m = m_base + 32 * b + l32;
+    if (m >= p.M) continue;
+    const int n = m / p.PQ;
+    const int pq = m - n * p.PQ;
+#pragma unroll
+    for (int a = 0; a < FK; ++a) {
+      const int kb = kb_base + a;
+      if (kb >= p.KBLK) continue;
+      int8_t *dst = y + ((size_t)(n * p.KBLK + kb) * p.PQ + pq) * 32 + 4 * half;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        uint32_t packed = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float f = (float)acc[a][b][4 * g + e];
+          f = f * alpha;
+          f = __builtin_rintf(f);
+          f = __builtin_fminf(__builtin_fmaxf(f, -128.0f), 127.0f);
+          packed |= ((uint32_t)(int)f & 0xffu) << (8 * e);
+        }
+        *reinterpret_cast<uint32_t *>(dst + 8 * g) = packed;
+      }
+    }
+  }
+}
+
+}  // namespace convfprop

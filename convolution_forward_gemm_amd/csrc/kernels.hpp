@@ -21,6 +21,13 @@ struct I8Params {
   int k_tiles;  // workgroup tiles along K
   uint32_t x_bytes, w_bytes;
   float alpha;
+  // Halo kernel only (see conv_i8_halo.hip): virtual rows per image, halo
+  // columns, halo DMA blocks per half-plane, LDS bytes per stage and total.
+  int N, HV, WV;
+  int halo_dpp;      // 1 KiB LDS-DMA blocks per half-plane
+  int halo_bytes;    // both half-planes
+  int stage_bytes;   // filter taps + halo of one channel block
+  int lds_bytes;     // dynamic LDS of one workgroup
 };
 
 typedef hipError_t (*I8LaunchFn)(const int8_t *x, const int8_t *w, int8_t *y,
@@ -35,12 +42,19 @@ struct I8Config {
   int kt;        // taps per stage
   int rs_outer;  // 1: needs (C/32) % kt == 0
   I8LaunchFn launch;
+  // Halo kernels (kind 1, 2): compiled filter size, waves, stages, and the
+  // most halo DMA blocks per wave per stage they can issue.
+  int kind;      // 0: per-tap fragment ring, 1: LDS activation halo + LDS
+                 // filter taps, 2: LDS activation halo + filter in registers
+  int fr, fs, nwaves, ns, hj;
 };
 
 // Host-only tables (not const: a const namespace-scope object would also be
 // emitted for the device and reference host launch functions).
 extern I8Config kI8Configs[];
 extern int kNumI8Configs;
+extern I8Config kI8HaloConfigs[];
+extern int kNumI8HaloConfigs;
 
 // Problem constants of the fp32 kernel.
 struct F32Params {

@@ -30,6 +30,7 @@ CONV_ERR_MISALIGNED = 4
 CONV_ERR_OVERFLOW_RISK = 5
 CONV_ERR_HIP = 6
 CONV_ERR_NO_MEMORY = 7
+CONV_ERR_INVALID_ALPHA = 8
 
 # conv_dtype_t / conv_layout_t
 CONV_DTYPE_INT8 = 0

@@ -49,6 +49,18 @@ def build_peak_probe(verbose: bool = False) -> str:
     return PEAK_PROBE
 
 
+def device_asm(source: str, verbose: bool = False) -> str:
+    """gfx950 assembly text of one source under the library's flags."""
+    import tempfile
+    flags = [f for f in FLAGS if f not in ("-fPIC", "-shared")]
+    with tempfile.TemporaryDirectory() as d:
+        out = os.path.join(d, "dev.s")
+        _run([HIPCC, *flags, "--cuda-device-only", "-S", os.path.join(CSRC, source), "-o", out],
+             verbose)
+        with open(out) as f:
+            return f.read()
+
+
 def build(verbose: bool = False) -> str:
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
     tmp = LIB + ".tmp%d" % os.getpid()

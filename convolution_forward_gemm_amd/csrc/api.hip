@@ -8,6 +8,7 @@
 // graph ("CUDA Graphs").  The operator shape (argument checks, then dispatch
 // of run-time types to compiled instantiations, then the kernel) is the one
 // the torchao PR 1515 review describes for CUTLASS-based operators.
+#include <math.h>
 #include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
@@ -214,6 +215,7 @@ const char *conv_status_string(conv_status_t s) {
     case CONV_ERR_OVERFLOW_RISK: return "CONV_ERR_OVERFLOW_RISK: C*R*S could overflow the int32 accumulator";
     case CONV_ERR_HIP: return "CONV_ERR_HIP: the HIP runtime reported an error";
     case CONV_ERR_NO_MEMORY: return "CONV_ERR_NO_MEMORY: host allocation failed";
+    case CONV_ERR_INVALID_ALPHA: return "CONV_ERR_INVALID_ALPHA: int8 alpha must be finite";
   }
   return "unknown conv_status_t";
 }
@@ -322,6 +324,7 @@ conv_status_t conv2d_fprop_run(conv2d_fprop_desc_t d, const void *x, const void 
   if (ranges_overlap(x, d->x_bytes, y, d->y_bytes) ||
       ranges_overlap(w, d->w_bytes, y, d->y_bytes))
     return CONV_ERR_UNSUPPORTED;
+  if (d->dtype == CONV_DTYPE_INT8 && !isfinite(alpha)) return CONV_ERR_INVALID_ALPHA;
   hipError_t e;
   if (d->dtype == CONV_DTYPE_INT8) {
     I8Params p = d->i8;

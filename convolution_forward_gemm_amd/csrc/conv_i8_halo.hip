@@ -258,11 +258,18 @@ conv_i8_halo_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ w,
 // unit, bound the all-LDS variant -- and shrinks a stage to the halo alone.
 //
 // Wait accounting: the halo LDS-DMAs and the filter loads share vmcnt, which
-// retires in issue order.  sched_barrier pins the order of the two streams,
-// so the number of loads issued after a stage's halo batch is known:
-//   prologue:  (NS-2)*HJ + AHEAD*FK
-//   boundary:  (NS-3)*HJ + min((NS-2)*RS, AHEAD+RS)*FK   (a lower bound that
-//              also holds in the first stages, fed by the prologue)
+// retires in issue order, so a wait for a halo batch may only count loads
+// that are certain to issue after that batch and before the wait.  The
+// compiler may move a filter load later (into the block that uses it) but
+// not earlier, so each count below is a lower bound under any such move:
+//   prologue (tap 0's filter loads, the halo batches of stages 0..NS-2,
+//   the wait, then the filter loads of taps 1..RS-2):
+//                             (NS-2)*HJ        -> stage 0 and tap 0 landed
+//   end of stage st (before issuing stage st+NS-1; stage st+1 must have
+//   landed):                  (NS-3)*HJ + RS*FK
+// The second counts the later halo batches plus the stage's own RS*FK
+// filter loads, which precede the wait in one straight-line block: the
+// stage loop has no conditional stage (an odd last stage runs after it).
 template <int WK, int WP, int FK, int FP, int R, int S, int NS, int HJ>
 struct HaloAdTile {
   static constexpr int NWAVES = WK * WP;
@@ -273,9 +280,8 @@ struct HaloAdTile {
   static constexpr int BN = 32 * PB;
   static constexpr int RS = R * S;
   static constexpr int AHEAD = RS - 1;
-  static constexpr int WAIT0 = (NS - 2) * HJ + AHEAD * FK;
-  static constexpr int WAITL =
-      (NS - 3) * HJ + ((NS - 2) * RS < AHEAD + RS ? (NS - 2) * RS : AHEAD + RS) * FK;
+  static constexpr int WAIT0 = (NS - 2) * HJ;
+  static constexpr int WAITL = (NS - 3) * HJ + RS * FK;
   static_assert(NS >= 3, "the ring needs a stage being read, one landed and one in flight");
   static_assert(WAIT0 < 64 && WAITL < 64, "vmcnt counts at most 63 outstanding loads");
 };
@@ -404,14 +410,15 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
 #pragma unroll
     for (int b = 0; b < FP; ++b) acc[a][b] = v16i{0};
 
+  load_a(0, aring[0]);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int s0 = 0; s0 < NS - 1; ++s0) issue_stage(s0);
   __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int g = 0; g < T::AHEAD; ++g) load_a(g, aring[g]);
-  __builtin_amdgcn_sched_barrier(0);
   halo_wait<T::WAIT0>();
   halo_barrier();
+#pragma unroll
+  for (int g = 1; g < T::AHEAD; ++g) load_a(g, aring[g]);
   read_b(0, 0, bf[0]);
 
   auto stage = [&](auto par_c, int st) {
@@ -449,10 +456,12 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
   if constexpr (T::RS % 2 == 0) {
     for (int st = 0; st < CB; ++st) stage(Par0{}, st);
   } else {
-    for (int st = 0; st < CB; st += 2) {
+    int st = 0;
+    for (; st + 1 < CB; st += 2) {
       stage(Par0{}, st);
-      if (st + 1 < CB) stage(Par1{}, st + 1);
+      stage(Par1{}, st + 1);
     }
+    if (st < CB) stage(Par0{}, st);
   }
   halo_wait<0>();
 

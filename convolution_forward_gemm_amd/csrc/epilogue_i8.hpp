@@ -8,12 +8,35 @@
 //   g = f * alpha  (one fp32 multiply; the build forbids FMA contraction)
 //   r = rint(g)    (round half to even)
 //   y = clamp(r, -128, 127)
+// The caller guarantees a finite alpha (the C ABI rejects others).
 #pragma once
 
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace convfprop {
+
+// The epilogue of one accumulator as fp32 bits whose low byte is the int8
+// result.  Clamping before rounding gives the same value as clamping after
+// it (the bounds are integers and rint is monotone), and adding 1.5 * 2^23
+// to a value in [-128, 127] rounds it to an integer, ties to even, exactly as
+// rint does (the sum's unit in the last place is 1), leaving that integer in
+// two's complement in the low mantissa bits.  Bit-identical to
+// clamp(rint(fl32(fl32(acc) * alpha))) for every finite alpha.
+__device__ __forceinline__ uint32_t i8_epilogue_bits(int acc, float alpha) {
+  const float f = (float)acc;
+  const float g = f * alpha;
+  const float c = __builtin_amdgcn_fmed3f(g, -128.0f, 127.0f);
+  return __builtin_bit_cast(uint32_t, c + 12582912.0f);
+}
+
+// Low bytes of four words, packed little-endian (v_perm_b32 byte selects).
+__device__ __forceinline__ uint32_t pack_low_bytes(uint32_t b0, uint32_t b1, uint32_t b2,
+                                                   uint32_t b3) {
+  const uint32_t lo = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u);
+  const uint32_t hi = __builtin_amdgcn_perm(b3, b2, 0x0c0c0400u);
+  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+}
 
 // Stores an FK x FP grid of 32x32 MFMA accumulator tiles (rows = output
 // channels, columns = output pixels) into y in NCxHWx<32> over K.
@@ -42,15 +65,10 @@ __device__ __forceinline__ void store_i8_tile(const v16i (&acc)[FK][FP], int8_t 
       int8_t *dst = y + ((size_t)(n * p.KBLK + kb) * p.PQ + pq) * 32 + 4 * half;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        uint32_t packed = 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float f = (float)acc[a][b][4 * g + e];
-          f = f * alpha;
-          f = __builtin_rintf(f);
-          f = __builtin_fminf(__builtin_fmaxf(f, -128.0f), 127.0f);
-          packed |= ((uint32_t)(int)f & 0xffu) << (8 * e);
-        }
+        const v16i &v = acc[a][b];
+        const uint32_t packed = pack_low_bytes(
+            i8_epilogue_bits(v[4 * g + 0], alpha), i8_epilogue_bits(v[4 * g + 1], alpha),
+            i8_epilogue_bits(v[4 * g + 2], alpha), i8_epilogue_bits(v[4 * g + 3], alpha));
         *reinterpret_cast<uint32_t *>(dst + 8 * g) = packed;
       }
     }

@@ -61,7 +61,8 @@ typedef enum {
     CONV_ERR_MISALIGNED = 4,     /* a device pointer breaks the required alignment */
     CONV_ERR_OVERFLOW_RISK = 5,  /* int8 C*R*S could overflow the int32 accumulator */
     CONV_ERR_HIP = 6,            /* the HIP runtime reported an error on launch   */
-    CONV_ERR_NO_MEMORY = 7       /* host allocation of the descriptor failed      */
+    CONV_ERR_NO_MEMORY = 7,      /* host allocation of the descriptor failed      */
+    CONV_ERR_INVALID_ALPHA = 8   /* int8 path: alpha is not a finite number       */
 } conv_status_t;
 
 typedef enum { CONV_DTYPE_INT8 = 0, CONV_DTYPE_FP32 = 1 } conv_dtype_t;
@@ -114,7 +115,9 @@ conv_status_t conv2d_fprop_desc_set_config(conv2d_fprop_desc_t desc, int config)
  *   x     device input  (layout per the descriptor)
  *   w     device filter (layout per the descriptor)
  *   y     device output (layout per the descriptor); fully overwritten
- *   alpha output scale (int8: applied before rounding; fp32: y = alpha*acc)
+ *   alpha output scale (int8: applied before rounding, must be finite --
+ *         an infinite or NaN alpha returns CONV_ERR_INVALID_ALPHA, since
+ *         0 * inf and NaN have no int8 value; fp32: y = alpha*acc, any value)
  * The int8 path needs x, w and y 16-byte aligned; the fp32 path 4-byte.
  * x and w must not overlap y. */
 conv_status_t conv2d_fprop_run(conv2d_fprop_desc_t desc, const void *x,

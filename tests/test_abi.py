@@ -38,7 +38,7 @@ def test_header_functions_are_exported(b):
 
 
 def test_status_strings(b):
-    for code in range(8):
+    for code in range(9):
         s = b.status_string(code)
         assert s and "unknown" not in s
     assert "unknown" in b.status_string(99)
@@ -131,6 +131,9 @@ def test_run_rejects_null_and_misaligned_before_launch(b):
     assert run(h, 4096, 1 << 16, (1 << 20) + 4, 1.0, None) == b.CONV_ERR_MISALIGNED
     # y overlapping x is rejected too (x: 2 KiB at 4096)
     assert run(h, 4096, 1 << 16, 4096 + 1024, 1.0, None) == b.CONV_ERR_UNSUPPORTED
+    # int8: an alpha without an int8 value is refused before any launch
+    for bad in (float("nan"), float("inf"), float("-inf")):
+        assert run(h, 4096, 1 << 16, 1 << 20, bad, None) == b.CONV_ERR_INVALID_ALPHA
     b.lib.conv2d_fprop_desc_destroy(h)
 
 

@@ -1,0 +1,153 @@
+"""Static check of the LDS-DMA ring's waits in the compiled int8 kernels.
+
+The int8 kernels stage operands through a ring of LDS buffers filled by
+LDS-DMA loads (buffer_load ... lds) and synchronise with a hand-placed
+`s_waitcnt vmcnt(N)` followed by `s_barrier`.  vmcnt counts every vector
+memory load and retires in issue order, so in a kernel that also loads into
+registers such a wait is only correct if, in the instruction order the
+compiler finally emits, every DMA of the stage about to be read lies more
+than N loads back.  The compiler may move ordinary loads between blocks (it
+once sank the prologue's filter loads behind the first wait), so this is
+checked on the emitted assembly: the prologue followed by several passes of
+the stage loop is replayed in text order and, at the j-th ring wait, every
+DMA of stages 0..j-1 must have retired.  A loop whose blocks the compiler
+laid out out of order fails the structural asserts rather than passing.
+
+No GPU is needed: hipcc cross-compiles the sources to gfx950 assembly.
+"""
+import os
+import re
+import shutil
+
+import pytest
+
+from convolution_forward_gemm_amd import build as hip_build
+
+pytestmark = pytest.mark.skipif(not os.path.exists(hip_build.HIPCC) and not shutil.which("hipcc"),
+                                reason="hipcc not available")
+
+VMEM = re.compile(r"^\s*(buffer_load|global_load|buffer_store|global_store|flat_)")
+WAIT = re.compile(r"^\s*s_waitcnt\s.*vmcnt\((\d+)\)")
+
+
+def _functions(asm, prefix):
+    """{mangled kernel name: [instruction lines]} for kernels matching prefix."""
+    out, cur, body = {}, None, []
+    for line in asm.splitlines():
+        m = re.match(r"^(_ZN9convfprop\w+):", line)
+        if m:
+            cur, body = m.group(1), []
+            continue
+        if cur is None:
+            continue
+        body.append(line)
+        if re.match(r"^\s*s_endpgm", line):
+            if cur.startswith(prefix):
+                out[cur] = body
+            cur = None
+    return out
+
+
+def _template_ints(name):
+    return [int(v) for v in re.findall(r"Li(\d+)E", name)]
+
+
+def _split(body):
+    """(prologue lines, loop-body lines): the body runs from the first loop
+    header label to the branch back to it."""
+    for i, line in enumerate(body):
+        m = re.match(r"^(\.LBB\w+):.*Loop Header", line)
+        if m:
+            label = m.group(1)
+            for j in range(i + 1, len(body)):
+                if re.match(r"^\s*s_c?branch\w*\s+%s\s*$" % re.escape(label), body[j]):
+                    return body[:i], body[i:j + 1]
+    return body, []
+
+
+def _events(lines):
+    """Sequence of ('load', is_dma) and ('ringwait', n) events."""
+    ev = []
+    instr = [l for l in lines if l.strip() and not l.strip().startswith(";")
+             and not re.match(r"^\s*\.", l) and not re.match(r"^\.LBB", l)]
+    for i, line in enumerate(instr):
+        if VMEM.match(line):
+            ev.append(("load", " lds" in line))
+        m = WAIT.match(line)
+        if m and i + 1 < len(instr) and re.match(r"^\s*s_barrier\b", instr[i + 1]):
+            ev.append(("ringwait", int(m.group(1))))
+    return ev
+
+
+def _check_kernel(name, body, ns):
+    pro, loop = _split(body)
+    pro_ev, loop_ev = _events(pro), _events(loop)
+    n_dma_pro = sum(1 for e in pro_ev if e == ("load", True))
+    assert n_dma_pro % (ns - 1) == 0, (name, n_dma_pro)
+    batch = n_dma_pro // (ns - 1)
+    assert batch > 0, name
+    assert loop_ev, "%s: no stage loop found" % name
+    seq = []            # per load: DMA batch index or None
+    dmas = 0
+    waits = 0
+    for kind, val in pro_ev + loop_ev * 4:
+        if kind == "load":
+            if val:
+                seq.append(dmas // batch)
+                dmas += 1
+            else:
+                seq.append(None)
+            continue
+        waits += 1
+        retired = len(seq) - val
+        pending = [b for b in seq[max(retired, 0):] if b is not None]
+        assert all(b >= waits for b in pending), (
+            "%s: ring wait %d (vmcnt(%d)) leaves a DMA of stage %d in flight"
+            % (name, waits, val, min(pending)))
+    assert waits >= 5, (name, waits)
+
+
+@pytest.fixture(scope="module")
+def halo_asm():
+    return hip_build.device_asm("conv_i8_halo.hip")
+
+
+def test_register_filter_kernels_ring_waits(halo_asm):
+    # The kernels that mix LDS-DMAs with ordinary loads into registers.  In
+    # the all-DMA kernels every vmcnt event is a DMA, and DMAs (LDS writes)
+    # keep their program order, so their counts cannot be disturbed.
+    fns = _functions(halo_asm, "_ZN9convfprop22conv_i8_halo_ad_kernel")
+    assert len(fns) >= 3
+    for name, body in fns.items():
+        ns = _template_ints(name)[6]    # <WK, WP, FK, FP, R, S, NS, HJ>
+        _check_kernel(name, body, ns)
+
+
+def test_checker_catches_a_wait_that_is_too_loose():
+    # Prologue: 2 stages of 2 DMAs in flight; vmcnt(3) lets stage 0's second
+    # DMA retire late, vmcnt(2) does not.  In the loop one register load
+    # follows the last batch, so vmcnt(1) covers stage 1 but vmcnt(2) would
+    # not.
+    body = [
+        "\tbuffer_load_dwordx4 v1, s[0:3], 0 offen lds",
+        "\tbuffer_load_dwordx4 v1, s[0:3], 0 offen lds",
+        "\tbuffer_load_dwordx4 v1, s[0:3], 0 offen lds",
+        "\tbuffer_load_dwordx4 v1, s[0:3], 0 offen lds",
+        "\ts_waitcnt vmcnt(3) lgkmcnt(0)",
+        "\ts_barrier",
+        ".LBB0_1:  ; =>This Inner Loop Header: Depth=1",
+        "\tbuffer_load_dwordx4 v[2:5], v1, s[0:3], 0 offen",
+        "\ts_waitcnt vmcnt(1) lgkmcnt(0)",
+        "\ts_barrier",
+        "\tbuffer_load_dwordx4 v1, s[0:3], 0 offen lds",
+        "\tbuffer_load_dwordx4 v1, s[0:3], 0 offen lds",
+        "\ts_cbranch_scc1 .LBB0_1",
+        "\ts_endpgm",
+    ]
+    with pytest.raises(AssertionError, match="ring wait 1"):
+        _check_kernel("synthetic", body, 3)
+    body[4] = "\ts_waitcnt vmcnt(2) lgkmcnt(0)"
+    _check_kernel("synthetic", body, 3)
+    body[8] = "\ts_waitcnt vmcnt(2) lgkmcnt(0)"
+    with pytest.raises(AssertionError, match="ring wait 2"):
+        _check_kernel("synthetic", body, 3)

@@ -41,8 +41,12 @@ __device__ __forceinline__ uint32_t pack_low_bytes(uint32_t b0, uint32_t b1, uin
 // Stores an FK x FP grid of 32x32 MFMA accumulator tiles (rows = output
 // channels, columns = output pixels) into y in NCxHWx<32> over K.
 // Accumulator layout of v_mfma_i32_32x32x32_i8: lane l, register i holds
-// D[row = 8*(i/4) + 4*(l/32) + i%4][col = l%32], so the quad i = 4g..4g+3 is
-// channels 8g + 4*(l/32) + 0..3 of pixel l%32: one packed 32-bit store.
+// D[row = 8*(i/4) + 4*(l/32) + i%4][col = l%32], so the quad i = 4g..4g+3
+// packs into the dword at byte 8g + 4*(l/32) of pixel l%32's 32 channels.
+// Lanes l and l+32 together hold a pixel's 32 bytes; two lane-half swaps
+// (v_permlane32_swap) give lane l bytes 0..15 and lane l+32 bytes 16..31,
+// so each tile leaves in one 16-byte store per lane: 32 consecutive pixels,
+// 1 KiB contiguous when they share an image.
 //   m_base: first pixel of fragment column 0; kb_base: first 32-channel
 //   block of fragment row 0.  Pixels past M and blocks past K/32 are skipped.
 template <int FK, int FP>
@@ -55,21 +59,27 @@ __device__ __forceinline__ void store_i8_tile(const v16i (&acc)[FK][FP], int8_t 
 #pragma unroll
   for (int b = 0; b < FP; ++b) {
     const int m = m_base + 32 * b + l32;
-    if (m >= p.M) continue;
     const int n = m / p.PQ;
     const int pq = m - n * p.PQ;
 #pragma unroll
     for (int a = 0; a < FK; ++a) {
-      const int kb = kb_base + a;
-      if (kb >= p.KBLK) continue;
-      int8_t *dst = y + ((size_t)(n * p.KBLK + kb) * p.PQ + pq) * 32 + 4 * half;
+      const v16i &v = acc[a][b];
+      uint32_t d[4];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const v16i &v = acc[a][b];
-        const uint32_t packed = pack_low_bytes(
-            i8_epilogue_bits(v[4 * g + 0], alpha), i8_epilogue_bits(v[4 * g + 1], alpha),
-            i8_epilogue_bits(v[4 * g + 2], alpha), i8_epilogue_bits(v[4 * g + 3], alpha));
-        *reinterpret_cast<uint32_t *>(dst + 8 * g) = packed;
+      for (int g = 0; g < 4; ++g)
+        d[g] = pack_low_bytes(i8_epilogue_bits(v[4 * g + 0], alpha),
+                              i8_epilogue_bits(v[4 * g + 1], alpha),
+                              i8_epilogue_bits(v[4 * g + 2], alpha),
+                              i8_epilogue_bits(v[4 * g + 3], alpha));
+      // (upper half of d0) <-> (lower half of d2), likewise d1 / d3; every
+      // lane takes part, before any per-lane predicate
+      const auto s02 = __builtin_amdgcn_permlane32_swap(d[0], d[2], false, false);
+      const auto s13 = __builtin_amdgcn_permlane32_swap(d[1], d[3], false, false);
+      const int kb = kb_base + a;
+      if (kb < p.KBLK && m < p.M) {
+        int8_t *dst = y + ((size_t)(n * p.KBLK + kb) * p.PQ + pq) * 32 + 16 * half;
+        *reinterpret_cast<v4i *>(dst) =
+            v4i{(int)s02[0], (int)s02[1], (int)s13[0], (int)s13[1]};
       }
     }
   }

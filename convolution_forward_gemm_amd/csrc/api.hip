@@ -60,12 +60,11 @@ const ShapeEntry kShapeTable[] = {
     {CONV_DTYPE_INT8, 1, 32, 8, 8, 32, 3, 3, 1, 1, 1, 1, 1, 1, 3},
     // int8 1x1 N2 C128 8x8 K128 (a 128x128x128 GEMM): many small tiles
     {CONV_DTYPE_INT8, 2, 128, 8, 8, 128, 1, 1, 0, 0, 1, 1, 1, 1, 14},
-    // int8 3x3 N32 C256 28x28 K256: activation halo in LDS, filter
-    // fragments in registers, 128 ch x 256 px tiles, 8 waves of 64x64
-    {CONV_DTYPE_INT8, 32, 256, 28, 28, 256, 3, 3, 1, 1, 1, 1, 1, 1, 20},
-    // int8 3x3 stride-2 N32 C128 56x56 K256: per-tap ring, 128 ch x 256 px
-    // tiles, 8 waves, 4 taps per stage, (r, s)-outer
-    {CONV_DTYPE_INT8, 32, 128, 56, 56, 256, 3, 3, 1, 1, 2, 2, 1, 1, 13},
+    // int8 3x3 N32 C256 28x28 K256 and the stride-2 N32 C128 56x56 K256:
+    // activation halo in LDS (row pitch 32 / 64 pixels), filter fragments in
+    // registers, 128 ch x 256 px tiles, 8 waves of 64x64
+    {CONV_DTYPE_INT8, 32, 256, 28, 28, 256, 3, 3, 1, 1, 1, 1, 1, 1, 30},
+    {CONV_DTYPE_INT8, 32, 128, 56, 56, 256, 3, 3, 1, 1, 2, 2, 1, 1, 32},
     {CONV_DTYPE_FP32, 8, 32, 512, 512, 64, 5, 9, 2, 4, 1, 1, 2, 3, 0},
 };
 
@@ -121,7 +120,9 @@ bool plan_halo(const conv2d_fprop_desc_s &d, const I8Config &c, int64_t M, I8Par
     const int64_t r = vrow(m1) - vrow(m0) + (int64_t)(d.R - 1) * d.dh + 1;
     if (r > rows) rows = r;
   }
-  const int64_t dpp = (rows * WV + 63) / 64;  // 1 KiB blocks per half-plane
+  if (c.pw > 0 && (WV > c.pw || d.dh != 1 || d.dw != 1)) return false;
+  const int64_t pitch = c.pw > 0 ? c.pw : WV;   // halo row pitch in LDS, pixels
+  const int64_t dpp = (rows * pitch + 63) / 64;  // 1 KiB blocks per half-plane
   const int64_t hblk = 2 * dpp;
   if ((hblk + c.nwaves - 1) / c.nwaves > c.hj) return false;
   // kind 1 stages the filter taps in LDS too; kind 2 keeps them in registers

@@ -270,7 +270,13 @@ conv_i8_halo_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ w,
 // The second counts the later halo batches plus the stage's own RS*FK
 // filter loads, which precede the wait in one straight-line block: the
 // stage loop has no conditional stage (an odd last stage runs after it).
-template <int WK, int WP, int FK, int FP, int R, int S, int NS, int HJ>
+//
+// PW > 0 fixes the halo's row pitch in LDS at PW pixels (>= the halo width)
+// and the dilation at 1, so every tap's offset inside the halo is a
+// compile-time constant: the LDS reads take it as an immediate and the
+// inner loop needs no address arithmetic.  PW = 0 keeps the pitch at the
+// halo width and any dilation.
+template <int WK, int WP, int FK, int FP, int R, int S, int NS, int HJ, int PW = 0>
 struct HaloAdTile {
   static constexpr int NWAVES = WK * WP;
   static constexpr int THREADS = 64 * NWAVES;
@@ -286,11 +292,11 @@ struct HaloAdTile {
   static_assert(WAIT0 < 64 && WAITL < 64, "vmcnt counts at most 63 outstanding loads");
 };
 
-template <int WK, int WP, int FK, int FP, int R, int S, int NS, int HJ>
+template <int WK, int WP, int FK, int FP, int R, int S, int NS, int HJ, int PW>
 __global__ void __launch_bounds__(64 * WK * WP)
 conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ w,
                        int8_t *__restrict__ y, I8Params p) {
-  using T = HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ>;
+  using T = HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ, PW>;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
 
   const int tid = threadIdx.x;
@@ -309,6 +315,7 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(w, p.w_bytes);
 
   const int HV = p.HV, WV = p.WV;
+  const int WVL = PW > 0 ? PW : WV;  // halo row pitch in LDS, pixels
   const int plane = p.halo_dpp * 1024;
   const int hblk = 2 * p.halo_dpp;
   unsigned char *dummy = lds + NS * p.stage_bytes;
@@ -328,13 +335,13 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
     if (g < hblk) {
       const int hp = g >= p.halo_dpp;
       const int slot = (g - hp * p.halo_dpp) * 64 + lane;
-      const int row = slot / WV;
-      const int col = slot - row * WV;
+      const int row = slot / WVL;
+      const int col = slot - row * WVL;
       const int v = v_lo + row;
       const int n = v / HV;
       const int ih = v - n * HV - p.ph;
       const int iw = col - p.pw;
-      if (n < p.N && (unsigned)ih < (unsigned)p.H && (unsigned)iw < (unsigned)p.W)
+      if (col < WV && n < p.N && (unsigned)ih < (unsigned)p.H && (unsigned)iw < (unsigned)p.W)
         off = (uint32_t)(((n * p.CB * p.H + ih) * p.W + iw) * 32 + hp * 16);
       dst = hp * plane + (g - hp * p.halo_dpp) * 1024;
     }
@@ -364,13 +371,14 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
       const int pq = m - n * p.PQ;
       const int op = pq / p.Q;
       const int oq = pq - op * p.Q;
-      a = ((n * HV + op * p.sh - v_lo) * WV + oq * p.sw) * 16;
+      a = ((n * HV + op * p.sh - v_lo) * WVL + oq * p.sw) * 16;
     }
     b_addr[i] = half * plane + a;
   }
   int tap_off[T::RS];
 #pragma unroll
-  for (int t = 0; t < T::RS; ++t) tap_off[t] = ((t / S) * p.dh * WV + (t % S) * p.dw) * 16;
+  for (int t = 0; t < T::RS; ++t)
+    tap_off[t] = PW > 0 ? ((t / S) * PW + (t % S)) * 16 : ((t / S) * p.dh * WV + (t % S) * p.dw) * 16;
 
   const int CB = p.CB;
   const int ntaps = CB * T::RS;
@@ -387,13 +395,13 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
     }
   };
 
-  // Filter fragments of global tap g = cb*RS + t into a register slot.
+  // Filter fragments of global tap g = cb*RS + t into a register slot; taps
+  // past the end (prefetched, never used) re-read the last one.
   v4i aring[T::RS][FK];
   auto load_a = [&](int g, v4i (&dst)[FK]) {
-    const bool live = g < ntaps;
+    const int soff = (g < ntaps ? g : ntaps - 1) * KB32;
 #pragma unroll
-    for (int i = 0; i < FK; ++i)
-      dst[i] = load_b128_s(wr, live ? a_off[i] : OOB_OFFSET, live ? g * KB32 : 0);
+    for (int i = 0; i < FK; ++i) dst[i] = load_b128_s(wr, a_off[i], soff);
   };
 
   v4i bf[2][FP];
@@ -417,8 +425,14 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
   __builtin_amdgcn_sched_barrier(0);
   halo_wait<T::WAIT0>();
   halo_barrier();
+  // In tap order, as in the loop: the compiler's own wait before each MFMA
+  // merges the prologue's load order into the loop's, so a shuffled
+  // prologue would shorten the filter prefetch in every stage.
 #pragma unroll
-  for (int g = 1; g < T::AHEAD; ++g) load_a(g, aring[g]);
+  for (int g = 1; g < T::AHEAD; ++g) {
+    load_a(g, aring[g]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   read_b(0, 0, bf[0]);
 
   auto stage = [&](auto par_c, int st) {
@@ -438,16 +452,19 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
         __builtin_amdgcn_sched_barrier(0);
         read_b(st + 1, 0, bf[nxt]);
       }
+      // Pixel-fragment-major order: fragment b of this tap is done after its
+      // FK MFMAs, and the next tap's fragment b is read into its registers
+      // right then, a whole tap ahead of its first use.
 #pragma unroll
-      for (int a = 0; a < FK; ++a)
+      for (int b = 0; b < FP; ++b)
 #pragma unroll
-        for (int b = 0; b < FP; ++b)
+        for (int a = 0; a < FK; ++a)
           acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(aring[t][a], bf[cur][b], acc[a][b], 0, 0, 0);
 #pragma unroll
-      for (int i = 0; i < FK * FP; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one filter load
+      for (int b = 0; b < FP; ++b) {
+        __builtin_amdgcn_sched_group_barrier(0x008, FK, 0);  // fragment b's MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+        if (b < FK) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one filter load
       }
     }
   };
@@ -468,15 +485,15 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
   store_i8_tile<FK, FP>(acc, y, p, m0 + 32 * wp * FP, k0 / 32 + wk * FK, lane);
 }
 
-template <int WK, int WP, int FK, int FP, int R, int S, int NS, int HJ>
+template <int WK, int WP, int FK, int FP, int R, int S, int NS, int HJ, int PW>
 static hipError_t launch_i8_halo_ad(const int8_t *x, const int8_t *w, int8_t *y,
                                     const I8Params &p, int grid, hipStream_t s) {
-  using T = HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ>;
+  using T = HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ, PW>;
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void *>(&conv_i8_halo_ad_kernel<WK, WP, FK, FP, R, S, NS, HJ>),
+      reinterpret_cast<const void *>(&conv_i8_halo_ad_kernel<WK, WP, FK, FP, R, S, NS, HJ, PW>),
       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((conv_i8_halo_ad_kernel<WK, WP, FK, FP, R, S, NS, HJ>), dim3(grid),
+  hipLaunchKernelGGL((conv_i8_halo_ad_kernel<WK, WP, FK, FP, R, S, NS, HJ, PW>), dim3(grid),
                      dim3(T::THREADS), p.lds_bytes, s, x, w, y, p);
   return hipGetLastError();
 }
@@ -502,12 +519,14 @@ static hipError_t launch_i8_halo(const int8_t *x, const int8_t *w, int8_t *y,
         &launch_i8_halo<WK, WP, FK, FP, R, S, NS, HJ>, 1, R, S, WK * WP, NS, HJ        \
   }
 
-#define I8_HALO_AD_CFG(WK, WP, FK, FP, R, S, NS, HJ)                                  \
+#define I8_HALO_AD_CFG(WK, WP, FK, FP, R, S, NS, HJ, PW)                              \
   I8Config {                                                                          \
-    "i8_halo_regfilter_mfma32x32x32_wg" #WK "x" #WP "_frag" #FK "x" #FP "_r" #R "s" #S "_ring" #NS, \
-        HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ>::BM, HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ>::BN, \
-        HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ>::THREADS, 0, R * S, 0,                \
-        &launch_i8_halo_ad<WK, WP, FK, FP, R, S, NS, HJ>, 2, R, S, WK * WP, NS, HJ     \
+    "i8_halo_regfilter_mfma32x32x32_wg" #WK "x" #WP "_frag" #FK "x" #FP "_r" #R "s" #S    \
+    "_ring" #NS "_hj" #HJ "_pitch" #PW,                                                 \
+        HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ, PW>::BM,                               \
+        HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ, PW>::BN,                               \
+        HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ, PW>::THREADS, 0, R * S, 0,             \
+        &launch_i8_halo_ad<WK, WP, FK, FP, R, S, NS, HJ, PW>, 2, R, S, WK * WP, NS, HJ, PW \
   }
 
 I8Config kI8HaloConfigs[] = {
@@ -516,11 +535,23 @@ I8Config kI8HaloConfigs[] = {
     I8_HALO_CFG(2, 2, 2, 2, 3, 3, 3, 6),  // 128 ch x 128 px, 4 waves of 64x64
     I8_HALO_CFG(1, 4, 2, 2, 3, 3, 3, 6),  // 64 ch x 256 px, 4 waves of 64x64
     // filter fragments in registers, LDS holds the halo only
-    I8_HALO_AD_CFG(2, 2, 2, 4, 3, 3, 4, 8),  // 128 ch x 256 px, 4 waves of 64x128
-    I8_HALO_AD_CFG(2, 4, 2, 2, 3, 3, 4, 4),  // 128 ch x 256 px, 8 waves of 64x64
-    I8_HALO_AD_CFG(2, 2, 2, 4, 3, 3, 3, 16), // 128 ch x 256 px, 4 waves, large halos
-    I8_HALO_AD_CFG(2, 2, 2, 2, 3, 3, 4, 8),  // 128 ch x 128 px, 4 waves of 64x64
-    I8_HALO_AD_CFG(2, 4, 2, 2, 3, 3, 3, 8),  // 128 ch x 256 px, 8 waves, large halos
+    I8_HALO_AD_CFG(2, 2, 2, 4, 3, 3, 4, 8, 0),  // 128 ch x 256 px, 4 waves of 64x128
+    I8_HALO_AD_CFG(2, 4, 2, 2, 3, 3, 4, 4, 0),  // 128 ch x 256 px, 8 waves of 64x64
+    I8_HALO_AD_CFG(2, 2, 2, 4, 3, 3, 3, 16, 0), // 128 ch x 256 px, 4 waves, large halos
+    I8_HALO_AD_CFG(2, 2, 2, 2, 3, 3, 4, 8, 0),  // 128 ch x 128 px, 4 waves of 64x64
+    I8_HALO_AD_CFG(2, 4, 2, 2, 3, 3, 3, 8, 0),  // 128 ch x 256 px, 8 waves, large halos
+    // halo DMA slots sized to the halo (few idle slots), deeper rings
+    I8_HALO_AD_CFG(2, 4, 2, 2, 3, 3, 4, 2, 0),
+    I8_HALO_AD_CFG(2, 4, 2, 2, 3, 3, 6, 2, 0),
+    I8_HALO_AD_CFG(2, 2, 2, 4, 3, 3, 4, 4, 0),
+    I8_HALO_AD_CFG(2, 2, 2, 4, 3, 3, 6, 4, 0),
+    I8_HALO_AD_CFG(2, 4, 2, 2, 3, 3, 3, 6, 0),
+    I8_HALO_AD_CFG(2, 2, 2, 4, 3, 3, 3, 11, 0),
+    // fixed LDS row pitch, dilation 1: immediate tap offsets
+    I8_HALO_AD_CFG(2, 4, 2, 2, 3, 3, 4, 2, 32),
+    I8_HALO_AD_CFG(2, 2, 2, 4, 3, 3, 4, 4, 32),
+    I8_HALO_AD_CFG(2, 4, 2, 2, 3, 3, 3, 6, 64),
+    I8_HALO_AD_CFG(2, 2, 2, 4, 3, 3, 3, 12, 64),
 };
 int kNumI8HaloConfigs = sizeof(kI8HaloConfigs) / sizeof(kI8HaloConfigs[0]);
 

@@ -47,6 +47,7 @@ struct I8Config {
   int kind;      // 0: per-tap fragment ring, 1: LDS activation halo + LDS
                  // filter taps, 2: LDS activation halo + filter in registers
   int fr, fs, nwaves, ns, hj;
+  int pw;  // kind 2: halo row pitch in LDS (0: the halo width; > 0: fixed, dilation 1)
 };
 
 // Host-only tables (not const: a const namespace-scope object would also be

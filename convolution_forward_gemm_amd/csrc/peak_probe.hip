@@ -34,6 +34,28 @@ __global__ void __launch_bounds__(256) mfma_i8(v16i *out, int iters) {
   out[blockIdx.x * 256 + t] = c0 + c1 + c2 + c3;
 }
 
+// Eight chains, operands rotating through registers as in the conv kernels'
+// inner loop (one wave per SIMD when launched with one workgroup per CU).
+__global__ void __launch_bounds__(256) mfma_i8_8chain(v16i *out, int iters) {
+  int t = threadIdx.x;
+  v4i a0 = {t, 1, 2, 3}, a1 = {t, 7, 2, 3}, b0 = {4, 5, 6, t}, b1 = {4, 9, 6, t};
+  v4i b2 = {1, 5, 6, t}, b3 = {4, 5, 3, t};
+  v16i c[8] = {};
+  for (int i = 0; i < iters; ++i) {
+    c[0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, b0, c[0], 0, 0, 0);
+    c[1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, b0, c[1], 0, 0, 0);
+    c[2] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, b1, c[2], 0, 0, 0);
+    c[3] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, b1, c[3], 0, 0, 0);
+    c[4] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, b2, c[4], 0, 0, 0);
+    c[5] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, b2, c[5], 0, 0, 0);
+    c[6] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, b3, c[6], 0, 0, 0);
+    c[7] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, b3, c[7], 0, 0, 0);
+  }
+  v16i s = {};
+  for (int k = 0; k < 8; ++k) s += c[k];
+  out[blockIdx.x * 256 + t] = s;
+}
+
 __global__ void __launch_bounds__(256) mfma_f32(v16f *out, int iters) {
   float a = threadIdx.x, b = 1.0f;
   v16f c0 = {}, c1 = {}, c2 = {}, c3 = {};
@@ -128,6 +150,20 @@ int main() {
   CHECK(hipEventElapsedTime(&ms, e0, e1));
   printf("int8 MFMA v_mfma_i32_32x32x32_i8 : %8.1f TOPS\n",
          2.0 * 32 * 32 * 32 * 4 * (double)iters * grid * 4 / ms / 1e9);
+
+  // one wave per SIMD (one workgroup of 4 waves per CU)
+  for (int chains : {4, 8}) {
+    CHECK(hipEventRecord(e0));
+    if (chains == 4)
+      hipLaunchKernelGGL(mfma_i8, dim3(ncu), dim3(256), 0, 0, (v16i *)out, iters);
+    else
+      hipLaunchKernelGGL(mfma_i8_8chain, dim3(ncu), dim3(256), 0, 0, (v16i *)out, iters / 2);
+    CHECK(hipEventRecord(e1));
+    CHECK(hipEventSynchronize(e1));
+    CHECK(hipEventElapsedTime(&ms, e0, e1));
+    printf("int8 MFMA, 1 wave/SIMD, %d chains : %8.1f TOPS\n", chains,
+           2.0 * 32 * 32 * 32 * 4 * (double)iters * ncu * 4 / ms / 1e9);
+  }
 
   CHECK(hipEventRecord(e0));
   hipLaunchKernelGGL(mfma_f32, dim3(grid), dim3(256), 0, 0, (v16f *)out, iters / 4);

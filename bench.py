@@ -25,10 +25,19 @@ METRIC = "int8 conv fprop TOPS (% of MFMA int8 peak); µs/call at smallest shape
 PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 MFMA, 5.0 POP/s
 PEAK_FP32_TFLOPS = 157.3     # MI355X fp32 MFMA
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "conv_i8_c3_traffic.json")
+PROFILES = os.path.join(ROOT, "profiles")
+# every source that shapes the int8 kernels' code or launch
 KERNEL_SOURCES = ["convolution_forward_gemm_amd/csrc/conv_i8.hip",
+                  "convolution_forward_gemm_amd/csrc/conv_i8_halo.hip",
+                  "convolution_forward_gemm_amd/csrc/epilogue_i8.hpp",
+                  "convolution_forward_gemm_amd/csrc/kernels.hpp",
                   "convolution_forward_gemm_amd/csrc/common.hpp",
-                  "convolution_forward_gemm_amd/csrc/api.hip"]
+                  "convolution_forward_gemm_amd/csrc/api.hip",
+                  "convolution_forward_gemm_amd/build.py"]
+
+
+def traffic_file(key: str) -> str:
+    return os.path.join(PROFILES, "conv_i8_%s_traffic.json" % key)
 
 
 def kernel_source_hash() -> str:
@@ -128,19 +137,161 @@ def cpu_baseline(wk, x, w):
         threads = min(threads, len(os.sched_getaffinity(0)))
     except AttributeError:
         pass
-    # Bounded sample: the first `n` images of the workload (all channels,
-    # all output pixels), about 10 s of CPU work at the expected rate.
-    n = max(1, min(wk.N, 8 * threads // 4))
+    # Bounded sample: whole passes over the workload (all images, channels and
+    # output pixels), repeated until about 10 s of CPU work (at most 30 passes);
+    # a pass over a few images when one full pass would take longer.
     t0 = time.perf_counter()
-    acc, y = oracle.conv2d_i8(x[:n], w, wk.alpha, **wk.conv_kwargs, nthreads=threads)
-    dt = time.perf_counter() - t0
+    acc, y = oracle.conv2d_i8(x[:1], w, wk.alpha, **wk.conv_kwargs, nthreads=threads)
+    per_image = time.perf_counter() - t0
+    n = wk.N if per_image * wk.N <= 10.0 else max(1, int(10.0 / per_image))
+    passes, dt = 0, 0.0
+    while passes < 30 and (passes == 0 or dt < 10.0):
+        t0 = time.perf_counter()
+        acc, y = oracle.conv2d_i8(x[:n], w, wk.alpha, **wk.conv_kwargs, nthreads=threads)
+        dt += time.perf_counter() - t0
+        passes += 1
     P, Q = acc.shape[2:]
-    ops = 2 * n * wk.K * P * Q * wk.C * wk.R * wk.S
+    ops = passes * 2 * n * wk.K * P * Q * wk.C * wk.R * wk.S
     return {"value": round(ops / dt / 1e12, 6), "unit": "TOPS", "cores": threads,
             "kind": "oracle",
-            "sample": "%d of %d images of the headline workload (all %d output channels, "
-                      "%dx%d outputs), int64 accumulation + epilogue; %.1f s"
-                      % (n, wk.N, wk.K, P, Q, dt)}
+            "sample": "%d pass(es) over %d of %d images of the headline workload (all %d output "
+                      "channels, %dx%d outputs), int64 accumulation + epilogue; %.1f s"
+                      % (passes, n, wk.N, wk.K, P, Q, dt)}
+
+
+# ---------------------------------------------------------------------------
+# Summaries of rocprofv3 output (run on the host after the profiled runs)
+# ---------------------------------------------------------------------------
+def _csv_rows(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _find(dirname, suffix):
+    for root, _, files in os.walk(dirname):
+        for fn in sorted(files):
+            if fn.endswith(suffix):
+                return os.path.join(root, fn)
+    raise FileNotFoundError("no *%s under %s" % (suffix, dirname))
+
+
+def _conv_kernel(names):
+    """The conv kernel among profiled kernel names (most dispatches wins)."""
+    conv = [n for n in names if "convfprop::conv_" in n]
+    if not conv:
+        raise ValueError("no conv kernel among %d profiled kernels" % len(names))
+    return max(conv, key=lambda n: names[n])
+
+
+def summarize_trace(key, trace_dir, command):
+    from convolution_forward_gemm_amd import workloads as wl
+    rows = _csv_rows(_find(trace_dir, "kernel_stats.csv"))
+    calls = {r["Name"]: int(r["Calls"]) for r in rows}
+    kname = _conv_kernel(calls)
+    lines = ["rocprofv3 kernel-trace summary: " + wl.WORKLOADS[key].name,
+             "command: " + command,
+             "kernel source hash (%s): %s" % (", ".join(os.path.basename(k) for k in KERNEL_SOURCES),
+                                             kernel_source_hash()),
+             "",
+             "%-100s %6s %12s %12s %12s %11s" % ("kernel", "calls", "avg_ns", "min_ns", "max_ns", "stddev_ns")]
+    for r in rows:
+        lines.append("%-100s %6d %12.1f %12d %12d %11.1f" % (
+            r["Name"][:100], int(r["Calls"]), float(r["AverageNs"]), int(float(r["MinNs"])),
+            int(float(r["MaxNs"])), float(r["StdDev"])))
+    avg = next(float(r["AverageNs"]) for r in rows if r["Name"] == kname)
+    wk = wl.WORKLOADS[key]
+    from convolution_forward_gemm_amd import binding as b
+    conv = b.Conv2dFprop(wk.N, wk.C, wk.H, wk.W, wk.K, wk.R, wk.S, pad=wk.pad,
+                         stride=wk.stride, dil=wk.dil, dtype=wk.dtype)
+    ops = conv_ops(wk, conv.P, conv.Q)
+    lines += ["", "conv kernel average %.2f us -> %.1f TOPS = %.1f%% of the %.1f POP/s int8 MFMA peak"
+              % (avg / 1e3, ops / avg / 1e3, 100 * ops / avg / 1e3 / PEAK_INT8_TOPS, PEAK_INT8_TOPS / 1e3)]
+    out = os.path.join(PROFILES, "conv_i8_%s_kernel_trace.txt" % key)
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return out
+
+
+def summarize_traffic(key, fetch_dir, write_dir, copy_mib, commands):
+    """HBM bytes per launch of the conv kernel: rocprofv3 FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch), each scaled by what the same counter reads
+    for a plain device copy of known size in the same process."""
+    from convolution_forward_gemm_amd import workloads as wl
+    from convolution_forward_gemm_amd import binding as b
+
+    def per_kernel(d, counter):
+        acc, cnt = {}, {}
+        for r in _csv_rows(_find(d, "counter_collection.csv")):
+            if r["Counter_Name"] != counter:
+                continue
+            acc[r["Kernel_Name"]] = acc.get(r["Kernel_Name"], 0.0) + float(r["Counter_Value"])
+            cnt[r["Kernel_Name"]] = cnt.get(r["Kernel_Name"], 0) + 1
+        return {k: acc[k] / cnt[k] for k in acc}, cnt
+
+    copy_bytes = copy_mib << 20
+    fetch, fcnt = per_kernel(fetch_dir, "FETCH_SIZE")
+    write, _ = per_kernel(write_dir, "WRITE_SIZE")
+    kname = _conv_kernel(fcnt)
+    copy_k = [k for k in fetch if "copyBuffer" in k or "copy" in k.lower() and "conv" not in k]
+    if not copy_k:
+        raise ValueError("the calibration copy kernel was not profiled")
+    ck = max(copy_k, key=lambda k: fetch[k])
+    f_factor = copy_bytes / (fetch[ck] * 1024)
+    w_factor = copy_bytes / (write[ck] * 1024)
+    rd = fetch[kname] * 1024 * f_factor
+    wr = write[kname] * 1024 * w_factor
+    wk = wl.WORKLOADS[key]
+    conv = b.Conv2dFprop(wk.N, wk.C, wk.H, wk.W, wk.K, wk.R, wk.S, pad=wk.pad,
+                         stride=wk.stride, dil=wk.dil, dtype=wk.dtype)
+    res = {
+        "workload": key, "workload_name": wk.name, "kernel": kname,
+        "kernel_config": conv.config, "kernel_source_hash": kernel_source_hash(),
+        "fetch_size_kib_per_dispatch_raw": round(fetch[kname], 1),
+        "write_size_kib_per_dispatch_raw": round(write[kname], 1),
+        "calibration": {"copy_bytes": copy_bytes, "copy_kernel": ck,
+                        "fetch_size_kib": round(fetch[ck], 1), "write_size_kib": round(write[ck], 1),
+                        "fetch_factor": round(f_factor, 4), "write_factor": round(w_factor, 4)},
+        "hbm_read_bytes_per_launch": int(rd), "hbm_write_bytes_per_launch": int(wr),
+        "hbm_bytes_per_launch": int(rd + wr),
+        "algorithmic_bytes_per_launch": conv_bytes(wk, conv.P, conv.Q, 1),
+        "commands": commands, "dispatches_averaged": fcnt[kname],
+    }
+    out = traffic_file(key)
+    with open(out, "w") as f:
+        json.dump(res, f, indent=1)
+    return out
+
+
+def summarize_counters(key, dirs, commands):
+    """Average per-dispatch value of every counter collected for the conv
+    kernel, over rocprofv3 --pmc runs of this script."""
+    from convolution_forward_gemm_amd import workloads as wl
+    acc, cnt, kname = {}, {}, None
+    for d in dirs:
+        rows = _csv_rows(_find(d, "counter_collection.csv"))
+        calls = {}
+        for r in rows:
+            calls[r["Kernel_Name"]] = calls.get(r["Kernel_Name"], 0) + 1
+        k = _conv_kernel(calls)
+        kname = kname or k
+        for r in rows:
+            if r["Kernel_Name"] == k:
+                acc[r["Counter_Name"]] = acc.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+                cnt[r["Counter_Name"]] = cnt.get(r["Counter_Name"], 0) + 1
+    lines = ["# conv kernel counters: " + wl.WORKLOADS[key].name, "",
+             "Kernel: `%s`" % kname,
+             "Kernel source hash (%s): %s" % (", ".join(os.path.basename(k) for k in KERNEL_SOURCES),
+                                              kernel_source_hash()),
+             "", "Commands (one rocprofv3 run per pass):", ""]
+    lines += ["    " + c for c in commands]
+    lines += ["", "| counter | per dispatch | dispatches |", "|---|---|---|"]
+    for c in sorted(acc):
+        lines.append("| %s | %.1f | %d |" % (c, acc[c] / cnt[c], cnt[c]))
+    out = os.path.join(PROFILES, "conv_i8_%s_counters.md" % key)
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return out
 
 
 def main():
@@ -154,7 +305,28 @@ def main():
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the timed region, run a plain device copy of this many MiB "
                          "(three times) to calibrate rocprofv3 FETCH_SIZE / WRITE_SIZE")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="write profiles/conv_i8_<workload>_kernel_trace.txt from a rocprofv3 "
+                         "--kernel-trace --stats output directory of this script, then exit")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/conv_i8_<workload>_traffic.json from rocprofv3 --pmc "
+                         "FETCH_SIZE and WRITE_SIZE runs of this script with --calib-copy-mib, then exit")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="DIR",
+                    help="write profiles/conv_i8_<workload>_counters.md from rocprofv3 --pmc "
+                         "output directories of this script, then exit")
+    ap.add_argument("--command", action="append", default=[],
+                    help="with --summarize-*: the profiling command(s) to record")
     args = ap.parse_args()
+    if args.summarize_counters:
+        print(summarize_counters(args.workload, args.summarize_counters, args.command))
+        return
+    if args.summarize_trace or args.summarize_traffic:
+        if args.summarize_trace:
+            print(summarize_trace(args.workload, args.summarize_trace, " && ".join(args.command)))
+        if args.summarize_traffic:
+            print(summarize_traffic(args.workload, *args.summarize_traffic,
+                                    args.calib_copy_mib or 256, args.command))
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
@@ -177,11 +349,15 @@ def main():
     ops = conv_ops(wk, conv.P, conv.Q)
     tops = ops / (ms * 1e-3) / 1e12
 
+    # HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    # summary, only while the kernel sources still match what was profiled
     traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        with open(TRAFFIC_FILE) as f:
+    tf = traffic_file(wk.key)
+    if os.path.exists(tf):
+        with open(tf) as f:
             tr = json.load(f)
-        if tr.get("kernel_source_hash") == kernel_source_hash() and tr.get("workload") == wk.key:
+        if (tr.get("kernel_source_hash") == kernel_source_hash() and tr.get("workload") == wk.key
+                and tr.get("kernel_config") == conv.config):
             traffic = tr.get("hbm_bytes_per_launch")
 
     out = {
@@ -202,6 +378,8 @@ def main():
                    "stride": list(wk.stride), "dilation": list(wk.dil),
                    "alpha": wk.alpha, "layout": "NCxHWx<32> / CxRSKx<32>",
                    "kernel_config": conv.config, "pct_of_int8_peak": round(100 * tops / PEAK_INT8_TOPS, 2)},
+        # achieved: algorithmic int8 ops of one launch / average launch time
+        # (HIP events on the launch stream over the timed region)
         "roofline": {"bound": "mfma", "achieved": round(tops, 3), "peak": PEAK_INT8_TOPS,
                      "unit": "TOPS", "frac": round(tops / PEAK_INT8_TOPS, 4),
                      "traffic": traffic,

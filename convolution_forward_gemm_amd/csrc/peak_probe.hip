@@ -56,6 +56,46 @@ __global__ void __launch_bounds__(256) mfma_i8_8chain(v16i *out, int iters) {
   out[blockIdx.x * 256 + t] = s;
 }
 
+// The same with K independent v_add_u32 issued by the wave after every
+// MFMA: how much vector ALU work one wave can hide behind its own MFMAs.
+template <int K>
+__global__ void __launch_bounds__(256) mfma_i8_valu(v16i *out, int *out2, int iters) {
+  int t = threadIdx.x;
+  v4i a0 = {t, 1, 2, 3}, a1 = {t, 7, 2, 3}, b0 = {4, 5, 6, t}, b1 = {4, 9, 6, t};
+  v16i c[8] = {};
+  int x[8];
+  for (int k = 0; k < 8; ++k) x[k] = t * (k + 1);
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      c[m] = __builtin_amdgcn_mfma_i32_32x32x32_i8((m & 1) ? a1 : a0, (m & 2) ? b1 : b0, c[m], 0, 0, 0);
+#pragma unroll
+      for (int k = 0; k < K; ++k) asm volatile("v_add_u32 %0, %0, %1" : "+v"(x[k % 8]) : "v"(t));
+    }
+  }
+  v16i s = {};
+  for (int k = 0; k < 8; ++k) s += c[k];
+  out[blockIdx.x * 256 + t] = s;
+  int xs = 0;
+  for (int k = 0; k < 8; ++k) xs += x[k];
+  out2[blockIdx.x * 256 + t] = xs;
+}
+
+// (A __global__ function's host-side address is a launch handle, not a
+// callable stub: each instantiation is launched by name.)
+template <int K>
+static int run_valu(int ncu, int iters, void *out, void *out2, hipEvent_t e0, hipEvent_t e1) {
+  CHECK(hipEventRecord(e0));
+  hipLaunchKernelGGL(mfma_i8_valu<K>, dim3(ncu), dim3(256), 0, 0, (v16i *)out, (int *)out2, iters);
+  CHECK(hipEventRecord(e1));
+  CHECK(hipEventSynchronize(e1));
+  float ms;
+  CHECK(hipEventElapsedTime(&ms, e0, e1));
+  printf("int8 MFMA, 1 wave/SIMD, %d v_add per MFMA : %8.1f TOPS\n", K,
+         2.0 * 32 * 32 * 32 * 8 * (double)iters * ncu * 4 / ms / 1e9);
+  return 0;
+}
+
 __global__ void __launch_bounds__(256) mfma_f32(v16f *out, int iters) {
   float a = threadIdx.x, b = 1.0f;
   v16f c0 = {}, c1 = {}, c2 = {}, c3 = {};
@@ -128,6 +168,7 @@ __global__ void copy_kernel(const v4i *__restrict__ in, v4i *__restrict__ out, s
 }
 
 int main() {
+  setvbuf(stdout, nullptr, _IOLBF, 0);  // each line reaches a redirected log at once
   hipDeviceProp_t prop;
   CHECK(hipGetDeviceProperties(&prop, 0));
   const int ncu = prop.multiProcessorCount;
@@ -163,6 +204,16 @@ int main() {
     CHECK(hipEventElapsedTime(&ms, e0, e1));
     printf("int8 MFMA, 1 wave/SIMD, %d chains : %8.1f TOPS\n", chains,
            2.0 * 32 * 32 * 32 * 4 * (double)iters * ncu * 4 / ms / 1e9);
+  }
+
+  // vector ALU work hidden behind one wave's own MFMAs
+  {
+    void *out2;
+    CHECK(hipMalloc(&out2, (size_t)ncu * 256 * 4));
+    if (run_valu<0>(ncu, iters / 8, out, out2, e0, e1) || run_valu<2>(ncu, iters / 8, out, out2, e0, e1) ||
+        run_valu<4>(ncu, iters / 8, out, out2, e0, e1) || run_valu<8>(ncu, iters / 8, out, out2, e0, e1))
+      return 1;
+    CHECK(hipFree(out2));
   }
 
   CHECK(hipEventRecord(e0));

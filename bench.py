@@ -29,6 +29,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 # every source that shapes the int8 kernels' code or launch
 KERNEL_SOURCES = ["convolution_forward_gemm_amd/csrc/conv_i8.hip",
                   "convolution_forward_gemm_amd/csrc/conv_i8_halo.hip",
+                  "convolution_forward_gemm_amd/csrc/conv_i8_small.hip",
                   "convolution_forward_gemm_amd/csrc/epilogue_i8.hpp",
                   "convolution_forward_gemm_amd/csrc/kernels.hpp",
                   "convolution_forward_gemm_amd/csrc/common.hpp",

@@ -47,25 +47,58 @@ bool ranges_overlap(const void *a, int64_t an, const void *b, int64_t bn) {
   return a0 < b0 + (uintptr_t)bn && b0 < a0 + (uintptr_t)an;
 }
 
-// Per-shape table: the configuration chosen for a problem by sweep.  Shapes
-// not listed fall back to the heuristic below.
+// int8 configurations: the per-tap ring kernels, the halo kernels, then the
+// one-pass kernels for small problems.
+int num_i8_configs() { return kNumI8Configs + kNumI8HaloConfigs + kNumI8SmallConfigs; }
+
+const I8Config *i8_config(int cfg) {
+  if (cfg < 0) return nullptr;
+  if (cfg < kNumI8Configs) return &kI8Configs[cfg];
+  cfg -= kNumI8Configs;
+  if (cfg < kNumI8HaloConfigs) return &kI8HaloConfigs[cfg];
+  cfg -= kNumI8HaloConfigs;
+  if (cfg < kNumI8SmallConfigs) return &kI8SmallConfigs[cfg];
+  return nullptr;
+}
+
+// Index of the configuration with this name, or -1.
+int find_config(conv_dtype_t dtype, const char *name) {
+  if (dtype == CONV_DTYPE_INT8) {
+    for (int i = 0; i < num_i8_configs(); ++i)
+      if (strcmp(i8_config(i)->name, name) == 0) return i;
+  } else {
+    for (int i = 0; i < kNumF32Configs; ++i)
+      if (strcmp(kF32Configs[i].name, name) == 0) return i;
+  }
+  return -1;
+}
+
+// Per-shape table: the configuration chosen for a problem by sweep, by
+// name.  Shapes not listed fall back to the heuristic below.
 struct ShapeEntry {
   conv_dtype_t dtype;
   int N, C, H, W, K, R, S, ph, pw, sh, sw, dh, dw;
-  int config;
+  const char *config;
 };
 
 const ShapeEntry kShapeTable[] = {
-    // int8 3x3 N1 C32 8x8 K32: launch-latency bound, one 32x32 tile per wave
-    {CONV_DTYPE_INT8, 1, 32, 8, 8, 32, 3, 3, 1, 1, 1, 1, 1, 1, 3},
-    // int8 1x1 N2 C128 8x8 K128 (a 128x128x128 GEMM): many small tiles
-    {CONV_DTYPE_INT8, 2, 128, 8, 8, 128, 1, 1, 0, 0, 1, 1, 1, 1, 14},
-    // int8 3x3 N32 C256 28x28 K256 and the stride-2 N32 C128 56x56 K256:
-    // activation halo in LDS (row pitch 32 / 64 pixels), filter fragments in
-    // registers, 128 ch x 256 px tiles, 8 waves of 64x64
-    {CONV_DTYPE_INT8, 32, 256, 28, 28, 256, 3, 3, 1, 1, 1, 1, 1, 1, 30},
-    {CONV_DTYPE_INT8, 32, 128, 56, 56, 256, 3, 3, 1, 1, 2, 2, 1, 1, 32},
-    {CONV_DTYPE_FP32, 8, 32, 512, 512, 64, 5, 9, 2, 4, 1, 1, 2, 3, 0},
+    // int8 3x3 N1 C32 8x8 K32 and 1x1 N2 C128 8x8 K128: launch-latency
+    // bound; one wave per 32x32 tile fetches its whole reduction in one
+    // memory round trip (one-pass kernel, rolled loops, small code)
+    {CONV_DTYPE_INT8, 1, 32, 8, 8, 32, 3, 3, 1, 1, 1, 1, 1, 1,
+     "i8_small_onepass_mfma32x32x32_frag1x1"},
+    {CONV_DTYPE_INT8, 2, 128, 8, 8, 128, 1, 1, 0, 0, 1, 1, 1, 1,
+     "i8_small_onepass_mfma32x32x32_frag1x1"},
+    // int8 3x3 N32 C256 28x28 K256: activation halo in LDS (row pitch 32),
+    // filter fragments in registers, 128 ch x 256 px tiles, 8 waves of 64x64
+    {CONV_DTYPE_INT8, 32, 256, 28, 28, 256, 3, 3, 1, 1, 1, 1, 1, 1,
+     "i8_halo_regfilter_mfma32x32x32_wg2x4_frag2x2_r3s3_ring4_hj2_pitch32_cps1"},
+    // int8 3x3 stride-2 N32 C128 56x56 K256: per-tap ring, 128 ch x 256 px,
+    // 8 waves, 4 taps per stage, (r, s)-outer
+    {CONV_DTYPE_INT8, 32, 128, 56, 56, 256, 3, 3, 1, 1, 2, 2, 1, 1,
+     "i8_mfma32x32x32_wg2x4_frag2x2_kt4_ring3_rsouter_true"},
+    {CONV_DTYPE_FP32, 8, 32, 512, 512, 64, 5, 9, 2, 4, 1, 1, 2, 3,
+     "f32_mfma32x32x2_frag2x2_cc4_depth3"},
 };
 
 int lookup_shape(const conv2d_fprop_desc_s &d) {
@@ -73,37 +106,36 @@ int lookup_shape(const conv2d_fprop_desc_s &d) {
     if (e.dtype == d.dtype && e.N == d.N && e.C == d.C && e.H == d.H && e.W == d.W &&
         e.K == d.K && e.R == d.R && e.S == d.S && e.ph == d.ph && e.pw == d.pw &&
         e.sh == d.sh && e.sw == d.sw && e.dh == d.dh && e.dw == d.dw)
-      return e.config;
+      return find_config(d.dtype, e.config);
   return -1;
 }
 
-int heuristic_i8(const conv2d_fprop_desc_s &d) {
-  const int64_t M = (int64_t)d.N * d.P * d.Q;
-  const int cb = d.C / 32;
-  if (M * d.K <= 128 * 128) return cb % 2 == 0 ? 14 : 3;  // latency-bound: small tiles
-  if (cb % 4 == 0) return 13;                             // (r, s)-outer, 4 taps per stage
-  if (cb % 2 == 0) return 11;                             // (r, s)-outer, 2 taps per stage
-  return 0;                                               // generic tap order
-}
-
-int heuristic_f32(const conv2d_fprop_desc_s &d) {
-  if (d.K <= 32) return 1;
-  return 0;
-}
+// Candidate configurations for shapes without a table entry, best first;
+// the first one that plans for the problem is used.
+const char *const kI8Candidates[] = {
+    // 3x3 (dilation 1): halo + register filter, then the all-LDS halo
+    "i8_halo_regfilter_mfma32x32x32_wg2x4_frag2x2_r3s3_ring4_hj2_pitch32_cps1",
+    "i8_halo_regfilter_mfma32x32x32_wg2x4_frag2x2_r3s3_ring3_hj6_pitch64_cps1",
+    "i8_halo_regfilter_mfma32x32x32_wg2x4_frag2x2_r3s3_ring4_hj2_pitch0_cps1",
+    "i8_halo_mfma32x32x32_wg2x4_frag2x2_r3s3_ring3",
+    "i8_halo_mfma32x32x32_wg1x4_frag2x2_r3s3_ring3",  // 64 output channels
+    // any shape: per-tap rings, (r, s)-outer when C/32 allows
+    "i8_mfma32x32x32_wg2x4_frag2x2_kt4_ring3_rsouter_true",
+    "i8_mfma32x32x32_wg2x4_frag2x2_kt2_ring6_rsouter_true",
+    "i8_mfma32x32x32_wg2x2_frag2x2_kt2_ring4_rsouter_false",
+    "i8_mfma32x32x32_wg1x4_frag2x1_kt4_ring4_rsouter_false",  // 64 ch x 128 px
+};
+const char *const kI8SmallCandidates[] = {
+    "i8_small_onepass_mfma32x32x32_frag1x1",
+    "i8_mfma32x32x32_wg1x2_frag1x1_kt4_ring4_rsouter_false",
+    "i8_mfma32x32x32_wg1x2_frag1x1_kt2_ring4_rsouter_true",
+    "i8_mfma32x32x32_wg1x1_frag1x1_kt2_ring4_rsouter_false",
+};
 
 int f32_lds_bytes(const conv2d_fprop_desc_s &d, int cfg) {
   return kF32Configs[cfg].lds_bytes * d.R * d.S;
 }
 
-// int8 configurations: the per-tap ring kernels, then the halo kernels.
-int num_i8_configs() { return kNumI8Configs + kNumI8HaloConfigs; }
-
-const I8Config *i8_config(int cfg) {
-  if (cfg < 0) return nullptr;
-  if (cfg < kNumI8Configs) return &kI8Configs[cfg];
-  if (cfg < num_i8_configs()) return &kI8HaloConfigs[cfg - kNumI8Configs];
-  return nullptr;
-}
 
 // Halo geometry of the LDS-halo kernel for this problem and tile width.
 // Returns false if its LDS or per-wave load budget does not fit.
@@ -127,7 +159,9 @@ bool plan_halo(const conv2d_fprop_desc_s &d, const I8Config &c, int64_t M, I8Par
   if ((hblk + c.nwaves - 1) / c.nwaves > c.hj) return false;
   // kind 1 stages the filter taps in LDS too; kind 2 keeps them in registers
   const int64_t filt = c.kind == 1 ? (int64_t)d.R * d.S * (c.bm / 32) * 1024 : 0;
-  const int64_t stage = filt + hblk * 1024;
+  const int64_t cps = c.kind == 2 && c.cps > 1 ? c.cps : 1;
+  if ((d.C / 32) % cps != 0) return false;
+  const int64_t stage = filt + hblk * 1024 * cps;
   const int64_t lds = c.ns * stage + 1024;
   if (lds > 160 * 1024) return false;
   if ((int64_t)d.N * HV > 0x7fffffff) return false;
@@ -172,7 +206,13 @@ bool plan(conv2d_fprop_desc_s &d, int cfg) {
     p.N = d.N;
     p.HV = p.WV = p.halo_dpp = p.halo_bytes = p.stage_bytes = 0;
     p.lds_bytes = c.lds_bytes;
-    if (c.kind != 0 && !plan_halo(d, c, M, p)) return false;
+    if ((c.kind == 1 || c.kind == 2) && !plan_halo(d, c, M, p)) return false;
+    if (c.kind == 3) {  // the whole reduction in LDS: ntaps filter + pixel fragments
+      // every fragment's DMA is in flight at once: at most 63 (vmcnt range)
+      const int64_t loads = (int64_t)p.ntaps * (1 + c.bn / 32);
+      if (loads > 63) return false;
+      p.lds_bytes = (int)(loads * 1024);
+    }
     d.grid = (int)(mt * kt);
   } else {
     if (cfg < 0 || cfg >= kNumF32Configs) return false;
@@ -264,9 +304,30 @@ conv_status_t conv2d_fprop_desc_create(conv2d_fprop_desc_t *out, int N, int C,
   d->w_bytes = wb;
   d->y_bytes = yb;
 
-  int cfg = lookup_shape(*d);
-  if (cfg < 0) cfg = dtype == CONV_DTYPE_INT8 ? heuristic_i8(*d) : heuristic_f32(*d);
-  bool ok = plan(*d, cfg);
+  bool ok = false;
+  const int cfg = lookup_shape(*d);
+  if (cfg >= 0) ok = plan(*d, cfg);
+  if (!ok && dtype == CONV_DTYPE_INT8) {
+    // Among the candidates that plan, the least estimated time: rounds of
+    // workgroups over the 256 CUs times the MFMA work of one tile (earlier
+    // candidates win ties).
+    const int64_t M = (int64_t)N * P * Q;
+    const bool small = M * K <= 128 * 128;
+    const char *const *cand = small ? kI8SmallCandidates : kI8Candidates;
+    const int nc = small ? (int)(sizeof(kI8SmallCandidates) / sizeof(kI8SmallCandidates[0]))
+                         : (int)(sizeof(kI8Candidates) / sizeof(kI8Candidates[0]));
+    int best = -1;
+    double best_cost = 0.0;
+    for (int i = 0; i < nc; ++i) {
+      const int c = find_config(dtype, cand[i]);
+      if (c < 0 || !plan(*d, c)) continue;
+      const I8Config &ic = *i8_config(c);
+      const double cost = (double)((d->grid + 255) / 256) * ic.bm * ic.bn;
+      if (best < 0 || cost < best_cost) best = c, best_cost = cost;
+    }
+    ok = best >= 0 && plan(*d, best);
+  }
+  if (!ok && dtype == CONV_DTYPE_FP32) ok = plan(*d, K <= 32 ? 1 : 0);
   if (!ok) {  // try every compiled configuration before giving up
     const int n = dtype == CONV_DTYPE_INT8 ? num_i8_configs() : kNumF32Configs;
     for (int c = 0; c < n && !ok; ++c) ok = plan(*d, c);

@@ -439,6 +439,13 @@ I8Config kI8Configs[] = {
     I8_CFG(4, 2, 2, 2, 2, 6, true),   // 12: 256 ch x 128 px, 8 waves of 64x64
     I8_CFG(2, 4, 2, 2, 4, 3, true),   // 13: 128 ch x 256 px, 8 waves, 4 taps per stage
     I8_CFG(1, 2, 1, 1, 2, 4, true),   // 14: 32 ch x 64 px, 2 waves
+    // tiny problems: every stage of a 3x3 / C32 reduction issued up front,
+    // so the operands arrive in one memory round trip
+    I8_CFG(1, 1, 1, 1, 4, 4, false),  // 15: 9 taps in 3 stages
+    I8_CFG(1, 2, 1, 1, 4, 4, false),  // 16: 32 ch x 64 px, 2 waves
+    I8_CFG(1, 1, 1, 1, 6, 3, false),  // 17: 9 taps in 2 stages
+    I8_CFG(1, 2, 1, 1, 6, 3, false),  // 18
+    I8_CFG(2, 2, 1, 1, 4, 4, true),   // 19: 64 ch x 64 px, 4 waves
 };
 int kNumI8Configs = sizeof(kI8Configs) / sizeof(kI8Configs[0]);
 

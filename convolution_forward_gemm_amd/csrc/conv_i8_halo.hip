@@ -276,7 +276,8 @@ conv_i8_halo_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ w,
 // compile-time constant: the LDS reads take it as an immediate and the
 // inner loop needs no address arithmetic.  PW = 0 keeps the pitch at the
 // halo width and any dilation.
-template <int WK, int WP, int FK, int FP, int R, int S, int NS, int HJ, int PW = 0>
+template <int WK, int WP, int FK, int FP, int R, int S, int NS, int HJ, int PW = 0,
+          int CPS = 1>
 struct HaloAdTile {
   static constexpr int NWAVES = WK * WP;
   static constexpr int THREADS = 64 * NWAVES;
@@ -286,17 +287,18 @@ struct HaloAdTile {
   static constexpr int BN = 32 * PB;
   static constexpr int RS = R * S;
   static constexpr int AHEAD = RS - 1;
-  static constexpr int WAIT0 = (NS - 2) * HJ;
-  static constexpr int WAITL = (NS - 3) * HJ + RS * FK;
+  static constexpr int TPS = RS * CPS;  // taps per stage
+  static constexpr int WAIT0 = (NS - 2) * HJ * CPS;
+  static constexpr int WAITL = (NS - 3) * HJ * CPS + TPS * FK;
   static_assert(NS >= 3, "the ring needs a stage being read, one landed and one in flight");
   static_assert(WAIT0 < 64 && WAITL < 64, "vmcnt counts at most 63 outstanding loads");
 };
 
-template <int WK, int WP, int FK, int FP, int R, int S, int NS, int HJ, int PW>
+template <int WK, int WP, int FK, int FP, int R, int S, int NS, int HJ, int PW, int CPS>
 __global__ void __launch_bounds__(64 * WK * WP)
 conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ w,
                        int8_t *__restrict__ y, I8Params p) {
-  using T = HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ, PW>;
+  using T = HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS>;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
 
   const int tid = threadIdx.x;
@@ -375,6 +377,12 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
     }
     b_addr[i] = half * plane + a;
   }
+  // the halo of the stage's c-th channel block sits c * halo_bytes further
+  int b_addr_c[CPS][FP];
+#pragma unroll
+  for (int c = 0; c < CPS; ++c)
+#pragma unroll
+    for (int i = 0; i < FP; ++i) b_addr_c[c][i] = b_addr[i] + c * p.halo_bytes;
   int tap_off[T::RS];
 #pragma unroll
   for (int t = 0; t < T::RS; ++t)
@@ -385,14 +393,18 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
   const int HW32 = p.HW * 32;
   const int KB32 = p.K * 32;
 
+  const int NST = CB / CPS;  // stages (the plan keeps CB a multiple of CPS)
+
   auto issue_stage = [&](int st) {
     unsigned char *base = lds + (st % NS) * p.stage_bytes;
-    const bool live = st < CB;
+    const bool live = st < NST;
 #pragma unroll
-    for (int j = 0; j < HJ; ++j) {
-      unsigned char *dst = hv_dst[j] >= 0 ? base + hv_dst[j] : dummy;
-      lds_dma16(xr, dst, live ? hv_off[j] : OOB_OFFSET, live ? st * HW32 : 0);
-    }
+    for (int c = 0; c < CPS; ++c)
+#pragma unroll
+      for (int j = 0; j < HJ; ++j) {
+        unsigned char *dst = hv_dst[j] >= 0 ? base + c * p.halo_bytes + hv_dst[j] : dummy;
+        lds_dma16(xr, dst, live ? hv_off[j] : OOB_OFFSET, live ? (st * CPS + c) * HW32 : 0);
+      }
   };
 
   // Filter fragments of global tap g = cb*RS + t into a register slot; taps
@@ -405,11 +417,11 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
   };
 
   v4i bf[2][FP];
-  auto read_b = [&](int st, int t, v4i (&b)[FP]) {
+  auto read_b = [&](int st, int t, v4i (&b)[FP]) {  // t: tap within the stage
     const unsigned char *base = lds + (st % NS) * p.stage_bytes;
 #pragma unroll
     for (int i = 0; i < FP; ++i)
-      b[i] = *reinterpret_cast<const v4i *>(base + b_addr[i] + tap_off[t]);
+      b[i] = *reinterpret_cast<const v4i *>(base + b_addr_c[t / T::RS][i] + tap_off[t % T::RS]);
   };
 
   v16i acc[FK][FP];
@@ -438,11 +450,11 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
   auto stage = [&](auto par_c, int st) {
     constexpr int PAR = decltype(par_c)::value;
 #pragma unroll
-    for (int t = 0; t < T::RS; ++t) {
+    for (int t = 0; t < T::TPS; ++t) {
       const int cur = (t + PAR) & 1;
       const int nxt = (t + 1 + PAR) & 1;
-      load_a(st * T::RS + t + T::AHEAD, aring[(t + T::AHEAD) % T::RS]);
-      if (t + 1 < T::RS) {
+      load_a(st * T::TPS + t + T::AHEAD, aring[(t + T::AHEAD) % T::RS]);
+      if (t + 1 < T::TPS) {
         read_b(st, t + 1, bf[nxt]);
       } else {
         __builtin_amdgcn_sched_barrier(0);
@@ -459,7 +471,8 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
       for (int b = 0; b < FP; ++b)
 #pragma unroll
         for (int a = 0; a < FK; ++a)
-          acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(aring[t][a], bf[cur][b], acc[a][b], 0, 0, 0);
+          acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(aring[t % T::RS][a], bf[cur][b],
+                                                            acc[a][b], 0, 0, 0);
 #pragma unroll
       for (int b = 0; b < FP; ++b) {
         __builtin_amdgcn_sched_group_barrier(0x008, FK, 0);  // fragment b's MFMAs
@@ -470,30 +483,30 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
   };
   using Par0 = std::integral_constant<int, 0>;
   using Par1 = std::integral_constant<int, 1>;
-  if constexpr (T::RS % 2 == 0) {
-    for (int st = 0; st < CB; ++st) stage(Par0{}, st);
+  if constexpr (T::TPS % 2 == 0) {
+    for (int st = 0; st < NST; ++st) stage(Par0{}, st);
   } else {
     int st = 0;
-    for (; st + 1 < CB; st += 2) {
+    for (; st + 1 < NST; st += 2) {
       stage(Par0{}, st);
       stage(Par1{}, st + 1);
     }
-    if (st < CB) stage(Par0{}, st);
+    if (st < NST) stage(Par0{}, st);
   }
   halo_wait<0>();
 
   store_i8_tile<FK, FP>(acc, y, p, m0 + 32 * wp * FP, k0 / 32 + wk * FK, lane);
 }
 
-template <int WK, int WP, int FK, int FP, int R, int S, int NS, int HJ, int PW>
+template <int WK, int WP, int FK, int FP, int R, int S, int NS, int HJ, int PW, int CPS>
 static hipError_t launch_i8_halo_ad(const int8_t *x, const int8_t *w, int8_t *y,
                                     const I8Params &p, int grid, hipStream_t s) {
-  using T = HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ, PW>;
+  using T = HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS>;
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void *>(&conv_i8_halo_ad_kernel<WK, WP, FK, FP, R, S, NS, HJ, PW>),
+      reinterpret_cast<const void *>(&conv_i8_halo_ad_kernel<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS>),
       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((conv_i8_halo_ad_kernel<WK, WP, FK, FP, R, S, NS, HJ, PW>), dim3(grid),
+  hipLaunchKernelGGL((conv_i8_halo_ad_kernel<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS>), dim3(grid),
                      dim3(T::THREADS), p.lds_bytes, s, x, w, y, p);
   return hipGetLastError();
 }
@@ -519,14 +532,15 @@ static hipError_t launch_i8_halo(const int8_t *x, const int8_t *w, int8_t *y,
         &launch_i8_halo<WK, WP, FK, FP, R, S, NS, HJ>, 1, R, S, WK * WP, NS, HJ        \
   }
 
-#define I8_HALO_AD_CFG(WK, WP, FK, FP, R, S, NS, HJ, PW)                              \
+#define I8_HALO_AD_CFG(WK, WP, FK, FP, R, S, NS, HJ, PW, CPS)                         \
   I8Config {                                                                          \
     "i8_halo_regfilter_mfma32x32x32_wg" #WK "x" #WP "_frag" #FK "x" #FP "_r" #R "s" #S    \
-    "_ring" #NS "_hj" #HJ "_pitch" #PW,                                                 \
-        HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ, PW>::BM,                               \
-        HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ, PW>::BN,                               \
-        HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ, PW>::THREADS, 0, R * S, 0,             \
-        &launch_i8_halo_ad<WK, WP, FK, FP, R, S, NS, HJ, PW>, 2, R, S, WK * WP, NS, HJ, PW \
+    "_ring" #NS "_hj" #HJ "_pitch" #PW "_cps" #CPS,                                     \
+        HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS>::BM,                          \
+        HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS>::BN,                          \
+        HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS>::THREADS, 0, R * S, 0,        \
+        &launch_i8_halo_ad<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS>, 2, R, S, WK * WP, NS, HJ, \
+        PW, CPS                                                                       \
   }
 
 I8Config kI8HaloConfigs[] = {
@@ -535,23 +549,31 @@ I8Config kI8HaloConfigs[] = {
     I8_HALO_CFG(2, 2, 2, 2, 3, 3, 3, 6),  // 128 ch x 128 px, 4 waves of 64x64
     I8_HALO_CFG(1, 4, 2, 2, 3, 3, 3, 6),  // 64 ch x 256 px, 4 waves of 64x64
     // filter fragments in registers, LDS holds the halo only
-    I8_HALO_AD_CFG(2, 2, 2, 4, 3, 3, 4, 8, 0),  // 128 ch x 256 px, 4 waves of 64x128
-    I8_HALO_AD_CFG(2, 4, 2, 2, 3, 3, 4, 4, 0),  // 128 ch x 256 px, 8 waves of 64x64
-    I8_HALO_AD_CFG(2, 2, 2, 4, 3, 3, 3, 16, 0), // 128 ch x 256 px, 4 waves, large halos
-    I8_HALO_AD_CFG(2, 2, 2, 2, 3, 3, 4, 8, 0),  // 128 ch x 128 px, 4 waves of 64x64
-    I8_HALO_AD_CFG(2, 4, 2, 2, 3, 3, 3, 8, 0),  // 128 ch x 256 px, 8 waves, large halos
+    I8_HALO_AD_CFG(2, 2, 2, 4, 3, 3, 4, 8, 0, 1),  // 128 ch x 256 px, 4 waves of 64x128
+    I8_HALO_AD_CFG(2, 4, 2, 2, 3, 3, 4, 4, 0, 1),  // 128 ch x 256 px, 8 waves of 64x64
+    I8_HALO_AD_CFG(2, 2, 2, 4, 3, 3, 3, 16, 0, 1), // 128 ch x 256 px, 4 waves, large halos
+    I8_HALO_AD_CFG(2, 2, 2, 2, 3, 3, 4, 8, 0, 1),  // 128 ch x 128 px, 4 waves of 64x64
+    I8_HALO_AD_CFG(2, 4, 2, 2, 3, 3, 3, 8, 0, 1),  // 128 ch x 256 px, 8 waves, large halos
     // halo DMA slots sized to the halo (few idle slots), deeper rings
-    I8_HALO_AD_CFG(2, 4, 2, 2, 3, 3, 4, 2, 0),
-    I8_HALO_AD_CFG(2, 4, 2, 2, 3, 3, 6, 2, 0),
-    I8_HALO_AD_CFG(2, 2, 2, 4, 3, 3, 4, 4, 0),
-    I8_HALO_AD_CFG(2, 2, 2, 4, 3, 3, 6, 4, 0),
-    I8_HALO_AD_CFG(2, 4, 2, 2, 3, 3, 3, 6, 0),
-    I8_HALO_AD_CFG(2, 2, 2, 4, 3, 3, 3, 11, 0),
+    I8_HALO_AD_CFG(2, 4, 2, 2, 3, 3, 4, 2, 0, 1),
+    I8_HALO_AD_CFG(2, 4, 2, 2, 3, 3, 6, 2, 0, 1),
+    I8_HALO_AD_CFG(2, 2, 2, 4, 3, 3, 4, 4, 0, 1),
+    I8_HALO_AD_CFG(2, 2, 2, 4, 3, 3, 6, 4, 0, 1),
+    I8_HALO_AD_CFG(2, 4, 2, 2, 3, 3, 3, 6, 0, 1),
+    I8_HALO_AD_CFG(2, 2, 2, 4, 3, 3, 3, 11, 0, 1),
     // fixed LDS row pitch, dilation 1: immediate tap offsets
-    I8_HALO_AD_CFG(2, 4, 2, 2, 3, 3, 4, 2, 32),
-    I8_HALO_AD_CFG(2, 2, 2, 4, 3, 3, 4, 4, 32),
-    I8_HALO_AD_CFG(2, 4, 2, 2, 3, 3, 3, 6, 64),
-    I8_HALO_AD_CFG(2, 2, 2, 4, 3, 3, 3, 12, 64),
+    I8_HALO_AD_CFG(2, 4, 2, 2, 3, 3, 4, 2, 32, 1),
+    I8_HALO_AD_CFG(2, 2, 2, 4, 3, 3, 4, 4, 32, 1),
+    I8_HALO_AD_CFG(2, 4, 2, 2, 3, 3, 3, 6, 64, 1),
+    I8_HALO_AD_CFG(2, 2, 2, 4, 3, 3, 3, 12, 64, 1),
+    // pitch = Q + 16 for Q = 28: a fragment that wraps to the next output
+    // row skips a multiple of 256 bytes and keeps its LDS banks
+    I8_HALO_AD_CFG(2, 4, 2, 2, 3, 3, 4, 3, 44, 1),
+    I8_HALO_AD_CFG(2, 2, 2, 4, 3, 3, 4, 5, 44, 1),
+    // two channel blocks per stage: half the ring waits and barriers
+    I8_HALO_AD_CFG(2, 4, 2, 2, 3, 3, 3, 2, 32, 2),
+    I8_HALO_AD_CFG(2, 4, 2, 2, 3, 3, 4, 2, 32, 2),
+    I8_HALO_AD_CFG(2, 2, 2, 4, 3, 3, 3, 4, 32, 2),
 };
 int kNumI8HaloConfigs = sizeof(kI8HaloConfigs) / sizeof(kI8HaloConfigs[0]);
 

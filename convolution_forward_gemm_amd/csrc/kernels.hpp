@@ -45,9 +45,11 @@ struct I8Config {
   // Halo kernels (kind 1, 2): compiled filter size, waves, stages, and the
   // most halo DMA blocks per wave per stage they can issue.
   int kind;      // 0: per-tap fragment ring, 1: LDS activation halo + LDS
-                 // filter taps, 2: LDS activation halo + filter in registers
+                 // filter taps, 2: LDS activation halo + filter in registers,
+                 // 3: one-pass kernel for small problems (whole reduction in LDS)
   int fr, fs, nwaves, ns, hj;
-  int pw;  // kind 2: halo row pitch in LDS (0: the halo width; > 0: fixed, dilation 1)
+  int pw;   // kind 2: halo row pitch in LDS (0: the halo width; > 0: fixed, dilation 1)
+  int cps;  // kind 2: channel blocks per ring stage (C/32 must be a multiple)
 };
 
 // Host-only tables (not const: a const namespace-scope object would also be
@@ -56,6 +58,8 @@ extern I8Config kI8Configs[];
 extern int kNumI8Configs;
 extern I8Config kI8HaloConfigs[];
 extern int kNumI8HaloConfigs;
+extern I8Config kI8SmallConfigs[];
+extern int kNumI8SmallConfigs;
 
 // Problem constants of the fp32 kernel.
 struct F32Params {

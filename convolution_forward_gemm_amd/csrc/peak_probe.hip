@@ -161,6 +161,13 @@ __global__ void __launch_bounds__(256) l2_to_lds(const char *src, int win, int i
   out[blockIdx.x * 256 + threadIdx.x] = acc;
 }
 
+// Launch floor: a kernel that does nothing, and one that copies 2 KiB from
+// HBM-resident memory (a tiny kernel's minimum: launch + one round trip).
+__global__ void empty_kernel() {}
+__global__ void tiny_copy(const v4i *__restrict__ in, v4i *__restrict__ out) {
+  out[threadIdx.x] = in[threadIdx.x];
+}
+
 __global__ void copy_kernel(const v4i *__restrict__ in, v4i *__restrict__ out, size_t n) {
   size_t i = blockIdx.x * (size_t)256 + threadIdx.x;
   size_t stride = (size_t)gridDim.x * 256;
@@ -277,5 +284,25 @@ int main() {
   CHECK(hipEventSynchronize(e1));
   CHECK(hipEventElapsedTime(&ms, e0, e1));
   printf("HBM copy 1 GiB (read + write)      : %8.1f GB/s\n", 5 * 2.0 * n * 16 / ms / 1e6);
+
+  // back-to-back launches on one stream, device time per launch
+  for (int kind = 0; kind < 2; ++kind) {
+    const int calls = 2000;
+    for (int i = 0; i < 50; ++i) {
+      if (kind == 0) hipLaunchKernelGGL(empty_kernel, dim3(1), dim3(64), 0, 0);
+      else hipLaunchKernelGGL(tiny_copy, dim3(1), dim3(128), 0, 0, (const v4i *)a, (v4i *)b);
+    }
+    CHECK(hipDeviceSynchronize());
+    CHECK(hipEventRecord(e0));
+    for (int i = 0; i < calls; ++i) {
+      if (kind == 0) hipLaunchKernelGGL(empty_kernel, dim3(1), dim3(64), 0, 0);
+      else hipLaunchKernelGGL(tiny_copy, dim3(1), dim3(128), 0, 0, (const v4i *)a, (v4i *)b);
+    }
+    CHECK(hipEventRecord(e1));
+    CHECK(hipEventSynchronize(e1));
+    CHECK(hipEventElapsedTime(&ms, e0, e1));
+    printf("%s, back-to-back       : %8.3f us per launch\n",
+           kind == 0 ? "empty kernel       " : "2 KiB copy kernel  ", ms * 1e3 / calls);
+  }
   return 0;
 }

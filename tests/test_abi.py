@@ -109,12 +109,29 @@ def test_output_dims_match_python_objects(b):
 
 
 def test_set_config(b):
-    c = b.Conv2dFprop(*GOOD[:7], pad=1)
+    # every compiled int8 configuration runs at least one of these shapes
+    # (a configuration may not fit a shape: its halo ring can exceed LDS);
+    # a refusal is CONV_ERR_UNSUPPORTED and leaves the descriptor usable
+    shapes = [b.Conv2dFprop(*GOOD[:7], pad=1),
+              b.Conv2dFprop(32, 128, 56, 56, 256, 3, 3, pad=1, stride=2),
+              b.Conv2dFprop(2, 256, 9, 7, 320, 3, 3, pad=1),
+              b.Conv2dFprop(1, 32, 8, 8, 32, 3, 3, pad=1)]
+    names = set()
     for i in range(b.num_configs("int8")):
-        c.set_config(i)
-        assert c.config.startswith("config=%d " % i)
+        ok = 0
+        for c in shapes:
+            try:
+                c.set_config(i)
+            except b.ConvError as e:
+                assert e.status == b.CONV_ERR_UNSUPPORTED
+                continue
+            assert c.config.startswith("config=%d " % i)
+            names.add(c.config.split()[1])
+            ok += 1
+        assert ok >= 1, "configuration %d runs none of the shapes" % i
+    assert len(names) == b.num_configs("int8"), "configuration names are not unique"
     with pytest.raises(b.ConvError):
-        c.set_config(b.num_configs("int8"))
+        shapes[0].set_config(b.num_configs("int8"))
     assert b.num_configs("fp32") >= 1
 
 
@@ -156,3 +173,21 @@ def test_binding_has_no_cpu_fallback():
         if name.endswith(".py"):
             text = open(os.path.join(ROOT, "convolution_forward_gemm_amd", name)).read()
             assert "import oracle" not in text and "from oracle" not in text, name
+
+
+def test_shape_table_choices(b):
+    # the per-shape table names configurations; a name that no longer exists
+    # would silently fall back to the heuristic
+    from convolution_forward_gemm_amd import workloads as wl
+    expect = {
+        "c1": "i8_small_onepass_mfma32x32x32_frag1x1",
+        "c2": "i8_small_onepass_mfma32x32x32_frag1x1",
+        "c3": "i8_halo_regfilter_mfma32x32x32_wg2x4_frag2x2_r3s3_ring4_hj2_pitch32_cps1",
+        "c4": "i8_mfma32x32x32_wg2x4_frag2x2_kt4_ring3_rsouter_true",
+        "c5": "f32_mfma32x32x2_frag2x2_cc4_depth3",
+    }
+    for key, name in expect.items():
+        w = wl.WORKLOADS[key]
+        c = b.Conv2dFprop(w.N, w.C, w.H, w.W, w.K, w.R, w.S, pad=w.pad, stride=w.stride,
+                          dil=w.dil, dtype=w.dtype)
+        assert c.config.split()[1] == name, (key, c.config)

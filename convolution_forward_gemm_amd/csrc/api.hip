@@ -93,10 +93,10 @@ const ShapeEntry kShapeTable[] = {
     // filter fragments in registers, 128 ch x 256 px tiles, 8 waves of 64x64
     {CONV_DTYPE_INT8, 32, 256, 28, 28, 256, 3, 3, 1, 1, 1, 1, 1, 1,
      "i8_halo_regfilter_mfma32x32x32_wg2x4_frag2x2_r3s3_ring4_hj2_pitch32_cps1"},
-    // int8 3x3 stride-2 N32 C128 56x56 K256: per-tap ring, 128 ch x 256 px,
-    // 8 waves, 4 taps per stage, (r, s)-outer
+    // int8 3x3 stride-2 N32 C128 56x56 K256: the same kernel with a 64-pixel
+    // halo row pitch and a 3-stage ring
     {CONV_DTYPE_INT8, 32, 128, 56, 56, 256, 3, 3, 1, 1, 2, 2, 1, 1,
-     "i8_mfma32x32x32_wg2x4_frag2x2_kt4_ring3_rsouter_true"},
+     "i8_halo_regfilter_mfma32x32x32_wg2x4_frag2x2_r3s3_ring3_hj6_pitch64_cps1"},
     {CONV_DTYPE_FP32, 8, 32, 512, 512, 64, 5, 9, 2, 4, 1, 1, 2, 3,
      "f32_mfma32x32x2_frag2x2_cc4_depth3"},
 };

@@ -262,14 +262,15 @@ conv_i8_halo_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ w,
 // that are certain to issue after that batch and before the wait.  The
 // compiler may move a filter load later (into the block that uses it) but
 // not earlier, so each count below is a lower bound under any such move:
-//   prologue (tap 0's filter loads, the halo batches of stages 0..NS-2,
-//   the wait, then the filter loads of taps 1..RS-2):
-//                             (NS-2)*HJ        -> stage 0 and tap 0 landed
+//   prologue (the filter loads of taps 0..RS-2, then the halo batches of
+//   stages 0..NS-2):          (NS-2)*HJ*CPS    -> stage 0 has landed (and
+//                             every filter load not moved behind the wait)
 //   end of stage st (before issuing stage st+NS-1; stage st+1 must have
-//   landed):                  (NS-3)*HJ + RS*FK
-// The second counts the later halo batches plus the stage's own RS*FK
-// filter loads, which precede the wait in one straight-line block: the
-// stage loop has no conditional stage (an odd last stage runs after it).
+//   landed):                  (NS-3)*HJ*CPS + TPS*FK
+// The second counts the later halo batches plus the stage's own TPS*FK
+// filter loads (TPS = R*S*CPS taps per stage), which precede the wait in one
+// straight-line block: the stage loop has no conditional stage (an odd last
+// stage runs after it).
 //
 // PW > 0 fixes the halo's row pitch in LDS at PW pixels (>= the halo width)
 // and the dilation at 1, so every tap's offset inside the halo is a
@@ -430,21 +431,20 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
 #pragma unroll
     for (int b = 0; b < FP; ++b) acc[a][b] = v16i{0};
 
-  load_a(0, aring[0]);
-  __builtin_amdgcn_sched_barrier(0);
+  // The first RS-1 taps' filter fragments go out first, in tap order (the
+  // compiler's own wait before each MFMA merges the prologue's load order
+  // into the loop's, so a shuffled prologue would shorten the filter
+  // prefetch in every stage); their latency overlaps the first halo's.
+#pragma unroll
+  for (int g = 0; g < T::AHEAD; ++g) {
+    load_a(g, aring[g]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 #pragma unroll
   for (int s0 = 0; s0 < NS - 1; ++s0) issue_stage(s0);
   __builtin_amdgcn_sched_barrier(0);
   halo_wait<T::WAIT0>();
   halo_barrier();
-  // In tap order, as in the loop: the compiler's own wait before each MFMA
-  // merges the prologue's load order into the loop's, so a shuffled
-  // prologue would shorten the filter prefetch in every stage.
-#pragma unroll
-  for (int g = 1; g < T::AHEAD; ++g) {
-    load_a(g, aring[g]);
-    __builtin_amdgcn_sched_barrier(0);
-  }
   read_b(0, 0, bf[0]);
 
   auto stage = [&](auto par_c, int st) {
@@ -483,19 +483,51 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
   };
   using Par0 = std::integral_constant<int, 0>;
   using Par1 = std::integral_constant<int, 1>;
+  // With one channel block per stage the last stage runs apart (below); the
+  // ring loop runs the others.
+  const int NRING = CPS == 1 ? NST - 1 : NST;
   if constexpr (T::TPS % 2 == 0) {
-    for (int st = 0; st < NST; ++st) stage(Par0{}, st);
+    for (int st = 0; st < NRING; ++st) stage(Par0{}, st);
   } else {
     int st = 0;
-    for (; st + 1 < NST; st += 2) {
+    for (; st + 1 < NRING; st += 2) {
       stage(Par0{}, st);
       stage(Par1{}, st + 1);
     }
-    if (st < NST) stage(Par0{}, st);
+    if (st < NRING) stage(Par0{}, st);
   }
-  halo_wait<0>();
 
-  store_i8_tile<FK, FP>(acc, y, p, m0 + 32 * wp * FP, k0 / 32 + wk * FK, lane);
+  const int m_wave = m0 + 32 * wp * FP;
+  const int kb_wave = k0 / 32 + wk * FK;
+  if constexpr (CPS == 1) {
+    // Last stage, pixel-fragment by pixel-fragment: once fragment b has all
+    // its taps, its epilogue (vector ALU work and the store) overlaps the
+    // MFMAs of fragment b+1.  The stage's halo landed at the previous
+    // stage's wait; the ring holds the filter of its taps 0..RS-2 and the
+    // last tap's is loaded here.
+    const int st = NST - 1;
+    load_a(st * T::TPS + T::AHEAD, aring[T::AHEAD % T::RS]);
+    const unsigned char *base = lds + (st % NS) * p.stage_bytes;
+#pragma unroll
+    for (int b = 0; b < FP; ++b) {
+      v4i bb[2];
+      bb[0] = *reinterpret_cast<const v4i *>(base + b_addr_c[0][b] + tap_off[0]);
+#pragma unroll
+      for (int t = 0; t < T::RS; ++t) {
+        if (t + 1 < T::RS)
+          bb[(t + 1) & 1] = *reinterpret_cast<const v4i *>(base + b_addr_c[0][b] + tap_off[t + 1]);
+#pragma unroll
+        for (int a = 0; a < FK; ++a)
+          acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(aring[t][a], bb[t & 1], acc[a][b], 0, 0, 0);
+      }
+#pragma unroll
+      for (int a = 0; a < FK; ++a) store_i8_frag(acc[a][b], y, p, m_wave + 32 * b, kb_wave + a, lane);
+    }
+    halo_wait<0>();  // no LDS-DMA (of the ring's idle stages) may outlive the workgroup
+  } else {
+    halo_wait<0>();
+    store_i8_tile<FK, FP>(acc, y, p, m_wave, kb_wave, lane);
+  }
 }
 
 template <int WK, int WP, int FK, int FP, int R, int S, int NS, int HJ, int PW, int CPS>

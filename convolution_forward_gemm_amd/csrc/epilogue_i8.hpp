@@ -49,40 +49,41 @@ __device__ __forceinline__ uint32_t pack_low_bytes(uint32_t b0, uint32_t b1, uin
 // 1 KiB contiguous when they share an image.
 //   m_base: first pixel of fragment column 0; kb_base: first 32-channel
 //   block of fragment row 0.  Pixels past M and blocks past K/32 are skipped.
+// One 32x32 accumulator tile (rows = output channels of 32-channel block
+// kb, columns = output pixels m_col .. m_col+31) into y in NCxHWx<32> over K.
+__device__ __forceinline__ void store_i8_frag(const v16i &v, int8_t *__restrict__ y,
+                                              const I8Params &p, int m_col, int kb, int lane) {
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+  const float alpha = p.alpha;
+  const int m = m_col + l32;
+  uint32_t d[4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+    d[g] = pack_low_bytes(i8_epilogue_bits(v[4 * g + 0], alpha), i8_epilogue_bits(v[4 * g + 1], alpha),
+                          i8_epilogue_bits(v[4 * g + 2], alpha), i8_epilogue_bits(v[4 * g + 3], alpha));
+  // (upper half of d0) <-> (lower half of d2), likewise d1 / d3; every lane
+  // takes part, before any per-lane predicate
+  const auto s02 = __builtin_amdgcn_permlane32_swap(d[0], d[2], false, false);
+  const auto s13 = __builtin_amdgcn_permlane32_swap(d[1], d[3], false, false);
+  if (kb < p.KBLK && m < p.M) {
+    const int n = m / p.PQ;
+    const int pq = m - n * p.PQ;
+    int8_t *dst = y + ((size_t)(n * p.KBLK + kb) * p.PQ + pq) * 32 + 16 * half;
+    *reinterpret_cast<v4i *>(dst) = v4i{(int)s02[0], (int)s02[1], (int)s13[0], (int)s13[1]};
+  }
+}
+
+// An FK x FP grid of tiles: fragment (a, b) covers channel block kb_base + a
+// and pixels m_base + 32*b ...
 template <int FK, int FP>
 __device__ __forceinline__ void store_i8_tile(const v16i (&acc)[FK][FP], int8_t *__restrict__ y,
                                               const I8Params &p, int m_base, int kb_base,
                                               int lane) {
-  const int half = lane >> 5;
-  const int l32 = lane & 31;
-  const float alpha = p.alpha;
 #pragma unroll
-  for (int b = 0; b < FP; ++b) {
-    const int m = m_base + 32 * b + l32;
-    const int n = m / p.PQ;
-    const int pq = m - n * p.PQ;
+  for (int b = 0; b < FP; ++b)
 #pragma unroll
-    for (int a = 0; a < FK; ++a) {
-      const v16i &v = acc[a][b];
-      uint32_t d[4];
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-        d[g] = pack_low_bytes(i8_epilogue_bits(v[4 * g + 0], alpha),
-                              i8_epilogue_bits(v[4 * g + 1], alpha),
-                              i8_epilogue_bits(v[4 * g + 2], alpha),
-                              i8_epilogue_bits(v[4 * g + 3], alpha));
-      // (upper half of d0) <-> (lower half of d2), likewise d1 / d3; every
-      // lane takes part, before any per-lane predicate
-      const auto s02 = __builtin_amdgcn_permlane32_swap(d[0], d[2], false, false);
-      const auto s13 = __builtin_amdgcn_permlane32_swap(d[1], d[3], false, false);
-      const int kb = kb_base + a;
-      if (kb < p.KBLK && m < p.M) {
-        int8_t *dst = y + ((size_t)(n * p.KBLK + kb) * p.PQ + pq) * 32 + 16 * half;
-        *reinterpret_cast<v4i *>(dst) =
-            v4i{(int)s02[0], (int)s02[1], (int)s13[0], (int)s13[1]};
-      }
-    }
-  }
+    for (int a = 0; a < FK; ++a) store_i8_frag(acc[a][b], y, p, m_base + 32 * b, kb_base + a, lane);
 }
 
 }  // namespace convfprop

@@ -217,7 +217,7 @@ bool plan(conv2d_fprop_desc_s &d, int cfg) {
   } else {
     if (cfg < 0 || cfg >= kNumF32Configs) return false;
     const F32Config &c = kF32Configs[cfg];
-    if (f32_lds_bytes(d, cfg) > 65536) return false;
+    if (f32_lds_bytes(d, cfg) > 160 * 1024) return false;
     const int64_t mt = (M + c.bn - 1) / c.bn, kt = (d.K + c.bm - 1) / c.bm;
     if (mt * kt > 0x7fffffff) return false;
     F32Params &p = d.f32;

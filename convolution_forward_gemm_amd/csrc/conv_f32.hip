@@ -17,8 +17,9 @@
 //     plane size to the offset.  Masked lanes read past the buffer end and
 //     get zeros.
 //   * Weights of a channel chunk are staged once per workgroup into LDS,
-//     transposed to [c][r][s][k] so that an MFMA operand is 32 consecutive
-//     floats (conflict-free ds_read_b32).  The activation operand is read
+//     transposed to [c][r][s][k] (row pitch BM+1) so that an MFMA operand is
+//     32 consecutive floats (conflict-free ds_read_b32); the staging reads
+//     each output channel's contiguous run of the chunk with whole waves.  The activation operand is read
 //     straight from global memory (L1/L2 serve the R*S-fold reuse), with a
 //     software pipeline of DEPTH taps in flight.
 #include "common.hpp"
@@ -33,7 +34,9 @@ struct F32Tile {
   static constexpr int BM = 32 * FK;           // output channels per workgroup
   static constexpr int BN = 32 * FP * NWAVES;  // output pixels per workgroup
   static constexpr int PAIRS = CC / 2;         // MFMAs per tap per fragment
+  static constexpr int LDP = BM + 1;           // LDS row pitch of the staged weights
   static_assert(CC % 2 == 0, "channel chunk must hold whole pairs");
+  static_assert(THREADS % 64 == 0 && BM % (THREADS / 64) == 0, "staging rows per pass");
 };
 
 template <int FK, int FP, int CC, int DEPTH>
@@ -42,7 +45,7 @@ conv_f32_kernel(const float *__restrict__ x, const float *__restrict__ w,
                 float *__restrict__ y, F32Params p) {
   using T = F32Tile<FK, FP, CC, DEPTH>;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
-  float *wl = reinterpret_cast<float *>(lds_raw);  // [CC][R][S][BM]
+  float *wl = reinterpret_cast<float *>(lds_raw);  // [CC][R][S][LDP]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -85,64 +88,91 @@ conv_f32_kernel(const float *__restrict__ x, const float *__restrict__ w,
 #pragma unroll
     for (int b = 0; b < FP; ++b) acc[a][b] = v16f{0.0f};
 
-  const int chunk_elems = CC * RS * T::BM;
+  const int crs = CC * RS;  // weights of one output channel in a chunk
   const float alpha = p.alpha;
 
   for (int c0 = 0; c0 < p.C; c0 += CC) {
     // ---- stage W[k0 .. k0+BM)[c0 .. c0+CC)[r][s] into LDS as [cc][r][s][k].
+    // For one output channel the chunk's CC*R*S weights are contiguous in
+    // global memory: a wave reads 64 consecutive of them (one row segment)
+    // and writes them down an LDS column; the odd row pitch BM+1 keeps
+    // those writes on 64 different banks.  No division per element.
     __syncthreads();
-    for (int e = tid; e < chunk_elems; e += T::THREADS) {
-      int kk = e % T::BM;
-      int rest = e / T::BM;  // = cc*RS + rs
-      int cc = rest / RS;
-      int rs = rest - cc * RS;
-      int k = k0 + kk, c = c0 + cc;
-      float v = 0.0f;
-      if (k < p.K && c < p.C) v = w[((size_t)k * p.C + c) * RS + rs];
-      wl[e] = v;
+    {
+      constexpr int ROWS = T::THREADS / 64;  // output channels per pass
+      const int jl = tid & 63;
+      const int kr = tid >> 6;
+      for (int j0 = 0; j0 < crs; j0 += 64) {
+        const int j = j0 + jl;
+        const int c = c0 + j / RS;
+#pragma unroll 4
+        for (int kk = kr; kk < T::BM; kk += ROWS) {
+          const int k = k0 + kk;
+          float v = 0.0f;
+          if (j < crs && k < p.K && c < p.C) v = w[((size_t)k * p.C + c0) * RS + j];
+          if (j < crs) wl[j * T::LDP + kk] = v;
+        }
+      }
     }
     __syncthreads();
 
     // ---- taps of this chunk, software-pipelined DEPTH deep ---------------
-    // Tap index tt = r*S + s.  For each tap, a lane loads T::PAIRS values per
-    // pixel fragment: channel c0 + 2*i + half for pair i.
+    // For each tap a lane loads T::PAIRS values per pixel fragment: channel
+    // c0 + 2*i + half for pair i.  The loader walks (r, s) incrementally.
+    // The tap loop is branch-free: it runs a whole number of DEPTH-blocks,
+    // and taps past R*S load zeros (and read the last tap's weights), so
+    // they add nothing.
+    uint32_t chan_off[T::PAIRS];
+    bool chan_ok[T::PAIRS];
+#pragma unroll
+    for (int i = 0; i < T::PAIRS; ++i) {
+      const int c = c0 + 2 * i + half;
+      chan_ok[i] = c < p.C;
+      chan_off[i] = (uint32_t)(c * p.HW);
+    }
     float ring[DEPTH][T::PAIRS][FP];
-    auto load_tap = [&](int tt, float (&dst)[T::PAIRS][FP]) {
-      int r = tt / p.S;
-      int s = tt - r * p.S;
+    int ld_r = 0, ld_s = 0, ld_tap = 0;
+    auto load_next = [&](float (&dst)[T::PAIRS][FP]) {
+      const bool live = ld_tap < RS;
+      const int rdh = ld_r * p.dh, sdw = ld_s * p.dw;
 #pragma unroll
       for (int b = 0; b < FP; ++b) {
-        int h = px_h0[b] + r * p.dh;
-        int ww = px_w0[b] + s * p.dw;
-        bool ok = (unsigned)h < (unsigned)p.H && (unsigned)ww < (unsigned)p.W;
-        int base = px_base[b] + r * p.dh * p.W + s * p.dw;
+        const int h = px_h0[b] + rdh;
+        const int ww = px_w0[b] + sdw;
+        // bitwise, not short-circuit, so that no branch is formed
+        const bool ok = live & ((unsigned)h < (unsigned)p.H) & ((unsigned)ww < (unsigned)p.W);
+        const uint32_t base = (uint32_t)(px_base[b] + rdh * p.W + sdw);
 #pragma unroll
-        for (int i = 0; i < T::PAIRS; ++i) {
-          int c = c0 + 2 * i + half;
-          uint32_t off = (ok && c < p.C) ? (uint32_t)(base + c * p.HW) * 4u : OOB_OFFSET;
-          dst[i][b] = load_f32(xr, off);
-        }
+        for (int i = 0; i < T::PAIRS; ++i)
+          dst[i][b] = load_f32(xr, (ok & chan_ok[i]) ? (base + chan_off[i]) * 4u : OOB_OFFSET);
+      }
+      ++ld_tap;
+      if (++ld_s == p.S) {
+        ld_s = 0;
+        ++ld_r;
       }
     };
 
 #pragma unroll
-    for (int d = 0; d < DEPTH - 1; ++d)
-      if (d < RS) load_tap(d, ring[d]);
+    for (int d = 0; d < DEPTH - 1; ++d) load_next(ring[d]);
 
-    for (int tt0 = 0; tt0 < RS; tt0 += DEPTH) {
+    const int rs_blocks = (RS + DEPTH - 1) / DEPTH;
+    for (int blk = 0; blk < rs_blocks; ++blk) {
 #pragma unroll
       for (int d = 0; d < DEPTH; ++d) {
-        const int tt = tt0 + d;
-        if (tt >= RS) break;
-        // prefetch tap tt + DEPTH - 1 into the slot freed last step
-        const int pf = tt + DEPTH - 1;
-        if (pf < RS) load_tap(pf, ring[(d + DEPTH - 1) % DEPTH]);
+        const int tt = blk * DEPTH + d;
+        // prefetch DEPTH-1 taps ahead into the slot freed last step; the
+        // scheduling barrier keeps the loads at the head of the tap (the
+        // scheduler would otherwise sink them next to their use)
+        load_next(ring[(d + DEPTH - 1) % DEPTH]);
+        __builtin_amdgcn_sched_barrier(0);
+        const int ttw = tt < RS ? tt : RS - 1;
 #pragma unroll
         for (int i = 0; i < T::PAIRS; ++i) {
           float af[FK];
 #pragma unroll
           for (int a = 0; a < FK; ++a)
-            af[a] = wl[((2 * i + half) * RS + tt) * T::BM + 32 * a + l32];
+            af[a] = wl[((2 * i + half) * RS + ttw) * T::LDP + 32 * a + l32];
 #pragma unroll
           for (int a = 0; a < FK; ++a)
 #pragma unroll
@@ -177,7 +207,11 @@ template <int FK, int FP, int CC, int DEPTH>
 static hipError_t launch_f32(const float *x, const float *w, float *y,
                              const F32Params &p, int grid, hipStream_t s) {
   using T = F32Tile<FK, FP, CC, DEPTH>;
-  const int lds = CC * p.R * p.S * T::BM * 4;
+  const int lds = CC * p.R * p.S * T::LDP * 4;
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void *>(&conv_f32_kernel<FK, FP, CC, DEPTH>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL((conv_f32_kernel<FK, FP, CC, DEPTH>), dim3(grid),
                      dim3(T::THREADS), lds, s, x, w, y, p);
   return hipGetLastError();
@@ -187,7 +221,7 @@ static hipError_t launch_f32(const float *x, const float *w, float *y,
   F32Config {                                                                  \
     "f32_mfma32x32x2_frag" #FK "x" #FP "_cc" #CC "_depth" #DEPTH,             \
         F32Tile<FK, FP, CC, DEPTH>::BM, F32Tile<FK, FP, CC, DEPTH>::BN, 256,   \
-        CC * 4 * F32Tile<FK, FP, CC, DEPTH>::BM, 0, &launch_f32<FK, FP, CC, DEPTH> \
+        CC * 4 * F32Tile<FK, FP, CC, DEPTH>::LDP, 0, &launch_f32<FK, FP, CC, DEPTH> \
   }
 
 // lds_bytes here is per filter tap (times R*S at launch).
@@ -195,6 +229,8 @@ F32Config kF32Configs[] = {
     F32_CFG(2, 2, 4, 3),  // 0: 64 ch x 256 px
     F32_CFG(1, 2, 4, 3),  // 1: 32 ch x 256 px
     F32_CFG(2, 1, 8, 3),  // 2: 64 ch x 128 px, 8-channel chunks
+    F32_CFG(2, 2, 4, 5),  // 3: 64 ch x 256 px, deeper activation prefetch
+    F32_CFG(2, 2, 4, 2),  // 4: 64 ch x 256 px, shallower prefetch
 };
 int kNumF32Configs = sizeof(kF32Configs) / sizeof(kF32Configs[0]);
 

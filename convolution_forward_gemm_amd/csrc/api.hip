@@ -97,8 +97,10 @@ const ShapeEntry kShapeTable[] = {
     // halo row pitch and a 3-stage ring
     {CONV_DTYPE_INT8, 32, 128, 56, 56, 256, 3, 3, 1, 1, 2, 2, 1, 1,
      "i8_halo_regfilter_mfma32x32x32_wg2x4_frag2x2_r3s3_ring3_hj6_pitch64_cps1"},
+    // fp32 5x9 dilated N8 C32 512x512 K64: 8 waves, 64 ch x 512 px per
+    // workgroup (half the weight staging per pixel of a 4-wave tile)
     {CONV_DTYPE_FP32, 8, 32, 512, 512, 64, 5, 9, 2, 4, 1, 1, 2, 3,
-     "f32_mfma32x32x2_frag2x2_cc4_depth3"},
+     "f32_mfma32x32x2_8waves_frag2x2_cc4_depth3"},
 };
 
 int lookup_shape(const conv2d_fprop_desc_s &d) {

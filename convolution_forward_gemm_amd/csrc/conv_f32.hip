@@ -27,10 +27,10 @@
 
 namespace convfprop {
 
-template <int FK, int FP, int CC, int DEPTH>
+template <int FK, int FP, int CC, int DEPTH, int NW = 4>
 struct F32Tile {
-  static constexpr int NWAVES = 4;
-  static constexpr int THREADS = 256;
+  static constexpr int NWAVES = NW;
+  static constexpr int THREADS = 64 * NW;
   static constexpr int BM = 32 * FK;           // output channels per workgroup
   static constexpr int BN = 32 * FP * NWAVES;  // output pixels per workgroup
   static constexpr int PAIRS = CC / 2;         // MFMAs per tap per fragment
@@ -39,11 +39,11 @@ struct F32Tile {
   static_assert(THREADS % 64 == 0 && BM % (THREADS / 64) == 0, "staging rows per pass");
 };
 
-template <int FK, int FP, int CC, int DEPTH>
-__global__ void __launch_bounds__(256)
+template <int FK, int FP, int CC, int DEPTH, int NW>
+__global__ void __launch_bounds__(64 * NW)
 conv_f32_kernel(const float *__restrict__ x, const float *__restrict__ w,
                 float *__restrict__ y, F32Params p) {
-  using T = F32Tile<FK, FP, CC, DEPTH>;
+  using T = F32Tile<FK, FP, CC, DEPTH, NW>;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
   float *wl = reinterpret_cast<float *>(lds_raw);  // [CC][R][S][LDP]
 
@@ -203,26 +203,33 @@ conv_f32_kernel(const float *__restrict__ x, const float *__restrict__ w,
   }
 }
 
-template <int FK, int FP, int CC, int DEPTH>
+template <int FK, int FP, int CC, int DEPTH, int NW>
 static hipError_t launch_f32(const float *x, const float *w, float *y,
                              const F32Params &p, int grid, hipStream_t s) {
-  using T = F32Tile<FK, FP, CC, DEPTH>;
+  using T = F32Tile<FK, FP, CC, DEPTH, NW>;
   const int lds = CC * p.R * p.S * T::LDP * 4;
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void *>(&conv_f32_kernel<FK, FP, CC, DEPTH>),
+      reinterpret_cast<const void *>(&conv_f32_kernel<FK, FP, CC, DEPTH, NW>),
       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((conv_f32_kernel<FK, FP, CC, DEPTH>), dim3(grid),
+  hipLaunchKernelGGL((conv_f32_kernel<FK, FP, CC, DEPTH, NW>), dim3(grid),
                      dim3(T::THREADS), lds, s, x, w, y, p);
   return hipGetLastError();
 }
 
-#define F32_CFG(FK, FP, CC, DEPTH)                                             \
-  F32Config {                                                                  \
-    "f32_mfma32x32x2_frag" #FK "x" #FP "_cc" #CC "_depth" #DEPTH,             \
-        F32Tile<FK, FP, CC, DEPTH>::BM, F32Tile<FK, FP, CC, DEPTH>::BN, 256,   \
-        CC * 4 * F32Tile<FK, FP, CC, DEPTH>::LDP, 0, &launch_f32<FK, FP, CC, DEPTH> \
+#define F32_CFG_W(FK, FP, CC, DEPTH, NW, NAME)                                       \
+  F32Config {                                                                        \
+    NAME, F32Tile<FK, FP, CC, DEPTH, NW>::BM, F32Tile<FK, FP, CC, DEPTH, NW>::BN, 64 * NW,  \
+        CC * 4 * F32Tile<FK, FP, CC, DEPTH, NW>::LDP, 0, &launch_f32<FK, FP, CC, DEPTH, NW> \
   }
+#define F32_CFG(FK, FP, CC, DEPTH) \
+  F32_CFG_W(FK, FP, CC, DEPTH, 4, "f32_mfma32x32x2_frag" #FK "x" #FP "_cc" #CC "_depth" #DEPTH)
+#define F32_CFG16(FK, FP, CC, DEPTH) \
+  F32_CFG_W(FK, FP, CC, DEPTH, 16,   \
+            "f32_mfma32x32x2_16waves_frag" #FK "x" #FP "_cc" #CC "_depth" #DEPTH)
+#define F32_CFG8(FK, FP, CC, DEPTH) \
+  F32_CFG_W(FK, FP, CC, DEPTH, 8,   \
+            "f32_mfma32x32x2_8waves_frag" #FK "x" #FP "_cc" #CC "_depth" #DEPTH)
 
 // lds_bytes here is per filter tap (times R*S at launch).
 F32Config kF32Configs[] = {
@@ -231,6 +238,11 @@ F32Config kF32Configs[] = {
     F32_CFG(2, 1, 8, 3),  // 2: 64 ch x 128 px, 8-channel chunks
     F32_CFG(2, 2, 4, 5),  // 3: 64 ch x 256 px, deeper activation prefetch
     F32_CFG(2, 2, 4, 2),  // 4: 64 ch x 256 px, shallower prefetch
+    F32_CFG8(2, 2, 4, 3),  // 5: 64 ch x 512 px, 8 waves: half the weight staging per pixel
+    F32_CFG8(2, 2, 2, 3),  // 6: the same with 2-channel chunks
+    F32_CFG16(2, 2, 4, 3), // 7: 64 ch x 1024 px, 16 waves
+    F32_CFG8(2, 2, 4, 5),  // 8: 8 waves, deeper activation prefetch
+    F32_CFG8(2, 2, 8, 3),  // 9: 8 waves, 8-channel chunks
 };
 int kNumF32Configs = sizeof(kF32Configs) / sizeof(kF32Configs[0]);
 

@@ -164,7 +164,15 @@ bool plan_halo(const conv2d_fprop_desc_s &d, const I8Config &c, int64_t M, I8Par
   const int64_t cps = c.kind == 2 && c.cps > 1 ? c.cps : 1;
   if ((d.C / 32) % cps != 0) return false;
   const int64_t stage = filt + hblk * 1024 * cps;
-  const int64_t lds = c.ns * stage + 1024;
+  int64_t lds = c.ns * stage + 1024;
+  // kind 2: the prologue stages the filter of taps 0..R*S-2 once in LDS, in
+  // the last ring slot (first written at the end of stage 0) if it fits there
+  const int64_t apro = c.kind == 2 ? (int64_t)(d.R * d.S - 1) * (c.bm / 32) * 1024 : 0;
+  int64_t pro_off = (c.ns - 1) * stage;
+  if (apro > stage) {
+    pro_off = lds;
+    lds += apro;
+  }
   if (lds > 160 * 1024) return false;
   if ((int64_t)d.N * HV > 0x7fffffff) return false;
   p.HV = (int)HV;
@@ -173,6 +181,7 @@ bool plan_halo(const conv2d_fprop_desc_s &d, const I8Config &c, int64_t M, I8Par
   p.halo_bytes = (int)(hblk * 1024);
   p.stage_bytes = (int)stage;
   p.lds_bytes = (int)lds;
+  p.pro_off = (int)pro_off;
   return true;
 }
 

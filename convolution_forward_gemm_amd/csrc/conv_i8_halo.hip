@@ -262,9 +262,12 @@ conv_i8_halo_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ w,
 // that are certain to issue after that batch and before the wait.  The
 // compiler may move a filter load later (into the block that uses it) but
 // not earlier, so each count below is a lower bound under any such move:
-//   prologue (the filter loads of taps 0..RS-2, then the halo batches of
-//   stages 0..NS-2):          (NS-2)*HJ*CPS    -> stage 0 has landed (and
-//                             every filter load not moved behind the wait)
+//   prologue (stage 0's halo batch and the filter of taps 0..RS-2, both
+//   by LDS-DMA; no register loads):
+//                             0                -> both have landed.  Stages
+//                             1..NS-2 are issued only after this wait, so at
+//                             kernel start stage 0 does not share the memory
+//                             system with the later stages' halos.
 //   end of stage st (before issuing stage st+NS-1; stage st+1 must have
 //   landed):                  (NS-3)*HJ*CPS + TPS*FK
 // The second counts the later halo batches plus the stage's own TPS*FK
@@ -289,7 +292,13 @@ struct HaloAdTile {
   static constexpr int RS = R * S;
   static constexpr int AHEAD = RS - 1;
   static constexpr int TPS = RS * CPS;  // taps per stage
-  static constexpr int WAIT0 = (NS - 2) * HJ * CPS;
+  static constexpr int WAIT0 = 0;
+  // The prologue brings the filter of taps 0..RS-2 into LDS once per
+  // workgroup (AHEAD*KB blocks of 1 KiB, AJ per wave) instead of once per
+  // wave: the waves that share output channels would otherwise each load it.
+  static constexpr int APRO_BLK = AHEAD * KB;
+  static constexpr int APRO_BYTES = APRO_BLK * 1024;
+  static constexpr int AJ = (APRO_BLK + NWAVES - 1) / NWAVES;
   static constexpr int WAITL = (NS - 3) * HJ * CPS + TPS * FK;
   static_assert(NS >= 3, "the ring needs a stage being read, one landed and one in flight");
   static_assert(WAIT0 < 64 && WAITL < 64, "vmcnt counts at most 63 outstanding loads");
@@ -431,20 +440,33 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
 #pragma unroll
     for (int b = 0; b < FP; ++b) acc[a][b] = v16i{0};
 
-  // The first RS-1 taps' filter fragments go out first, in tap order (the
-  // compiler's own wait before each MFMA merges the prologue's load order
-  // into the loop's, so a shuffled prologue would shorten the filter
-  // prefetch in every stage); their latency overlaps the first halo's.
+  // Prologue: stage 0's halo and the filter of taps 0..RS-2 (block
+  // g = tap*KB + kb at pro_off + g KiB, the MFMA operand order), then the
+  // other stages once those have landed.  pro_off is a ring slot that is
+  // first written at the end of stage 0, or space of its own.
+  issue_stage(0);
+  unsigned char *apro = lds + p.pro_off;
 #pragma unroll
-  for (int g = 0; g < T::AHEAD; ++g) {
-    load_a(g, aring[g]);
-    __builtin_amdgcn_sched_barrier(0);
+  for (int j = 0; j < T::AJ; ++j) {
+    const int g = j * T::NWAVES + wave;
+    const int tap = g / T::KB;
+    const int kb = g - tap * T::KB;
+    const int k = k0 + 32 * kb + l32;
+    const bool ok = g < T::APRO_BLK;
+    lds_dma16(wr, ok ? apro + g * 1024 : dummy,
+              ok && k < p.K ? (uint32_t)(k * 32 + 16 * half) : OOB_OFFSET, ok ? tap * KB32 : 0);
   }
-#pragma unroll
-  for (int s0 = 0; s0 < NS - 1; ++s0) issue_stage(s0);
   __builtin_amdgcn_sched_barrier(0);
   halo_wait<T::WAIT0>();
   halo_barrier();
+#pragma unroll
+  for (int s0 = 1; s0 < NS - 1; ++s0) issue_stage(s0);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int g = 0; g < T::AHEAD; ++g)
+#pragma unroll
+    for (int i = 0; i < FK; ++i)
+      aring[g][i] = *reinterpret_cast<const v4i *>(apro + ((g * T::KB + wk * FK + i) * 64 + lane) * 16);
   read_b(0, 0, bf[0]);
 
   auto stage = [&](auto par_c, int st) {

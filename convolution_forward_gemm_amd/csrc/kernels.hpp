@@ -28,6 +28,7 @@ struct I8Params {
   int halo_bytes;    // both half-planes
   int stage_bytes;   // filter taps + halo of one channel block
   int lds_bytes;     // dynamic LDS of one workgroup
+  int pro_off;       // register-filter kernel: LDS offset of the prologue's filter taps
 };
 
 typedef hipError_t (*I8LaunchFn)(const int8_t *x, const int8_t *w, int8_t *y,

@@ -56,6 +56,30 @@ __global__ void __launch_bounds__(256) mfma_i8_8chain(v16i *out, int iters) {
   out[blockIdx.x * 256 + t] = s;
 }
 
+// Eight chains whose operands are uniform random int8 (read from a buffer)
+// and change from one MFMA to the next, as real data does.  The matrix
+// unit's rate depends on the operand bits: the constant, mostly-zero
+// operands above run faster than data like the conv workloads'.
+__global__ void __launch_bounds__(256) mfma_i8_rand(const v4i *__restrict__ src, v16i *out, int iters) {
+  int t = threadIdx.x;
+  v4i a[4], b[4];
+  for (int k = 0; k < 4; ++k) {
+    a[k] = src[(k * 256 + t) & 2047];
+    b[k] = src[((k + 4) * 256 + t) & 2047];
+  }
+  v16i c[8] = {};
+  for (int i = 0; i < iters; i += 4) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        c[j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[(j + u) & 3], b[((j >> 1) + u) & 3], c[j], 0, 0, 0);
+  }
+  v16i s = {};
+  for (int k = 0; k < 8; ++k) s += c[k];
+  out[blockIdx.x * 256 + t] = s;
+}
+
 // The same with K independent v_add_u32 issued by the wave after every
 // MFMA: how much vector ALU work one wave can hide behind its own MFMAs.
 template <int K>
@@ -211,6 +235,34 @@ int main() {
     CHECK(hipEventElapsedTime(&ms, e0, e1));
     printf("int8 MFMA, 1 wave/SIMD, %d chains : %8.1f TOPS\n", chains,
            2.0 * 32 * 32 * 32 * 4 * (double)iters * ncu * 4 / ms / 1e9);
+  }
+
+  // uniform random operands, on every CU and on 196 (the c3 grid)
+  {
+    v4i *rnd;
+    CHECK(hipMalloc(&rnd, 2048 * sizeof(v4i)));
+    static int host[2048 * 4];
+    unsigned st = 12345u;
+    for (int i = 0; i < 2048 * 4; ++i) {
+      st = st * 1664525u + 1013904223u;
+      host[i] = (int)st;
+    }
+    CHECK(hipMemcpy(rnd, host, sizeof(host), hipMemcpyHostToDevice));
+    const int rit = iters / 2;  // a multiple of 4
+    for (int g : {ncu, ncu < 196 ? ncu : 196}) {
+      hipLaunchKernelGGL(mfma_i8_rand, dim3(g), dim3(256), 0, 0, (const v4i *)rnd, (v16i *)out, 100);
+      CHECK(hipDeviceSynchronize());
+      CHECK(hipEventRecord(e0));
+      for (int r = 0; r < 4; ++r)
+        hipLaunchKernelGGL(mfma_i8_rand, dim3(g), dim3(256), 0, 0, (const v4i *)rnd, (v16i *)out, rit);
+      CHECK(hipEventRecord(e1));
+      CHECK(hipEventSynchronize(e1));
+      CHECK(hipEventElapsedTime(&ms, e0, e1));
+      const double tops = 4 * 2.0 * 32 * 32 * 32 * 8 * (double)rit * g * 4 / ms / 1e9;
+      printf("int8 MFMA, random operands, %3d CUs : %8.1f TOPS (%.1f per-CU rate x %d CUs)\n", g, tops,
+             tops / g * ncu, ncu);
+    }
+    CHECK(hipFree(rnd));
   }
 
   // vector ALU work hidden behind one wave's own MFMAs

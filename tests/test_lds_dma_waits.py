@@ -79,12 +79,15 @@ def _events(lines):
     return ev
 
 
-def _check_kernel(name, body, ns):
+def _check_kernel(name, body, ns, extra0=0):
+    """extra0: DMAs that follow stage 0's batch in the prologue and must have
+    landed at the first wait too (the register-filter kernel's prologue
+    filter taps)."""
     pro, loop = _split(body)
     pro_ev, loop_ev = _events(pro), _events(loop)
     n_dma_pro = sum(1 for e in pro_ev if e == ("load", True))
-    assert n_dma_pro % (ns - 1) == 0, (name, n_dma_pro)
-    batch = n_dma_pro // (ns - 1)
+    assert (n_dma_pro - extra0) % (ns - 1) == 0, (name, n_dma_pro)
+    batch = (n_dma_pro - extra0) // (ns - 1)
     assert batch > 0, name
     assert loop_ev, "%s: no stage loop found" % name
     seq = []            # per load: DMA batch index or None
@@ -93,7 +96,7 @@ def _check_kernel(name, body, ns):
     for kind, val in pro_ev + loop_ev * 4:
         if kind == "load":
             if val:
-                seq.append(dmas // batch)
+                seq.append(0 if dmas < batch + extra0 else (dmas - extra0) // batch)
                 dmas += 1
             else:
                 seq.append(None)
@@ -119,8 +122,10 @@ def test_register_filter_kernels_ring_waits(halo_asm):
     fns = _functions(halo_asm, "_ZN9convfprop22conv_i8_halo_ad_kernel")
     assert len(fns) >= 3
     for name, body in fns.items():
-        ns = _template_ints(name)[6]    # <WK, WP, FK, FP, R, S, NS, HJ>
-        _check_kernel(name, body, ns)
+        wk, wp, fk, _, r, s, ns = _template_ints(name)[:7]  # <WK, WP, FK, FP, R, S, NS, HJ, ...>
+        # the prologue's filter taps 0..R*S-2: (R*S-1)*WK*FK blocks over WK*WP waves
+        aj = ((r * s - 1) * wk * fk + wk * wp - 1) // (wk * wp)
+        _check_kernel(name, body, ns, aj)
 
 
 def test_checker_catches_a_wait_that_is_too_loose():
@@ -151,3 +156,24 @@ def test_checker_catches_a_wait_that_is_too_loose():
     body[8] = "\ts_waitcnt vmcnt(2) lgkmcnt(0)"
     with pytest.raises(AssertionError, match="ring wait 2"):
         _check_kernel("synthetic", body, 3)
+
+
+def test_checker_counts_prologue_extras_into_stage_0():
+    # Stage 0 (1 DMA) plus one extra DMA that must land with it, then stage 1.
+    body = [
+        "\tbuffer_load_dwordx4 v1, s[0:3], 0 offen lds",
+        "\tbuffer_load_dwordx4 v1, s[4:7], 0 offen lds",
+        "\ts_waitcnt vmcnt(0) lgkmcnt(0)",
+        "\ts_barrier",
+        "\tbuffer_load_dwordx4 v1, s[0:3], 0 offen lds",
+        ".LBB0_1:  ; =>This Inner Loop Header: Depth=1",
+        "\ts_waitcnt vmcnt(0) lgkmcnt(0)",
+        "\ts_barrier",
+        "\tbuffer_load_dwordx4 v1, s[0:3], 0 offen lds",
+        "\ts_cbranch_scc1 .LBB0_1",
+        "\ts_endpgm",
+    ]
+    _check_kernel("synthetic", body, 3, extra0=1)
+    body[2] = "\ts_waitcnt vmcnt(1) lgkmcnt(0)"   # the extra DMA may still be in flight
+    with pytest.raises(AssertionError, match="ring wait 1"):
+        _check_kernel("synthetic", body, 3, extra0=1)

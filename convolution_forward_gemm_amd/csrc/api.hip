@@ -83,8 +83,9 @@ struct ShapeEntry {
 
 const ShapeEntry kShapeTable[] = {
     // int8 3x3 N1 C32 8x8 K32 and 1x1 N2 C128 8x8 K128: launch-latency
-    // bound; one wave per 32x32 tile fetches its whole reduction in one
-    // memory round trip (one-pass kernel, rolled loops, small code)
+    // bound, chosen by back-to-back time per call (graph replay); one wave
+    // per 32x32 tile fetches its whole reduction in one memory round trip
+    // (one-pass kernel, rolled loops, small code)
     {CONV_DTYPE_INT8, 1, 32, 8, 8, 32, 3, 3, 1, 1, 1, 1, 1, 1,
      "i8_small_onepass_mfma32x32x32_frag1x1"},
     {CONV_DTYPE_INT8, 2, 128, 8, 8, 128, 1, 1, 0, 0, 1, 1, 1, 1,
@@ -159,15 +160,17 @@ bool plan_halo(const conv2d_fprop_desc_s &d, const I8Config &c, int64_t M, I8Par
   const int64_t dpp = (rows * pitch + 63) / 64;  // 1 KiB blocks per half-plane
   const int64_t hblk = 2 * dpp;
   if ((hblk + c.nwaves - 1) / c.nwaves > c.hj) return false;
-  // kind 1 stages the filter taps in LDS too; kind 2 keeps them in registers
-  const int64_t filt = c.kind == 1 ? (int64_t)d.R * d.S * (c.bm / 32) * 1024 : 0;
+  // kind 1 (and kind 2 with al) stages the filter taps of a stage's channel
+  // blocks in LDS too; kind 2 otherwise keeps them in registers
   const int64_t cps = c.kind == 2 && c.cps > 1 ? c.cps : 1;
   if ((d.C / 32) % cps != 0) return false;
+  const int64_t filt =
+      c.kind == 1 || (c.kind == 2 && c.al) ? (int64_t)d.R * d.S * (c.bm / 32) * 1024 * cps : 0;
   const int64_t stage = filt + hblk * 1024 * cps;
   int64_t lds = c.ns * stage + 1024;
   // kind 2: the prologue stages the filter of taps 0..R*S-2 once in LDS, in
   // the last ring slot (first written at the end of stage 0) if it fits there
-  const int64_t apro = c.kind == 2 ? (int64_t)(d.R * d.S - 1) * (c.bm / 32) * 1024 : 0;
+  const int64_t apro = c.kind == 2 && !c.al ? (int64_t)(d.R * d.S - 1) * (c.bm / 32) * 1024 : 0;
   int64_t pro_off = (c.ns - 1) * stage;
   if (apro > stage) {
     pro_off = lds;

@@ -280,8 +280,19 @@ conv_i8_halo_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ w,
 // compile-time constant: the LDS reads take it as an immediate and the
 // inner loop needs no address arithmetic.  PW = 0 keeps the pitch at the
 // halo width and any dilation.
+//
+// AL = 1 moves the filter operand into the ring too: each stage also holds
+// the filter of its TPS taps for the workgroup's KB channel blocks (block
+// t*KB + kb, 1 KiB, MFMA operand order), brought in by LDS-DMA once per
+// workgroup, and the waves read both operands from LDS one tap ahead.  The
+// waves that share output channels then no longer each pull the same
+// filter bytes from L2 (WP copies per workgroup), at the cost of LDS reads.
+// With no register loads, every vmcnt event is an LDS-DMA.  The NB DMAs of
+// stage st+NS-1 go out one per tap during stage st (its ring slot held
+// stage st-1, which the barrier at the end of stage st-1 released), so the
+// wait at the end of stage st counts NS-2 whole batches.
 template <int WK, int WP, int FK, int FP, int R, int S, int NS, int HJ, int PW = 0,
-          int CPS = 1>
+          int CPS = 1, int AL = 0>
 struct HaloAdTile {
   static constexpr int NWAVES = WK * WP;
   static constexpr int THREADS = 64 * NWAVES;
@@ -298,17 +309,23 @@ struct HaloAdTile {
   // wave: the waves that share output channels would otherwise each load it.
   static constexpr int APRO_BLK = AHEAD * KB;
   static constexpr int APRO_BYTES = APRO_BLK * 1024;
-  static constexpr int AJ = (APRO_BLK + NWAVES - 1) / NWAVES;
-  static constexpr int WAITL = (NS - 3) * HJ * CPS + TPS * FK;
+  static constexpr int AJ = AL ? 0 : (APRO_BLK + NWAVES - 1) / NWAVES;
+  // AL = 1: filter blocks per stage and filter DMAs per wave per stage
+  static constexpr int FBLK = TPS * KB;
+  static constexpr int FJ = AL ? (FBLK + NWAVES - 1) / NWAVES : 0;
+  // AL = 1: DMAs per wave per stage; they go out one per tap through the
+  // stage NS-1 ahead (its slot was freed by the previous stage barrier)
+  static constexpr int NB = HJ * CPS + FJ;
+  static constexpr int WAITL = AL ? (NS - 2) * NB : (NS - 3) * HJ * CPS + TPS * FK;
   static_assert(NS >= 3, "the ring needs a stage being read, one landed and one in flight");
   static_assert(WAIT0 < 64 && WAITL < 64, "vmcnt counts at most 63 outstanding loads");
 };
 
-template <int WK, int WP, int FK, int FP, int R, int S, int NS, int HJ, int PW, int CPS>
+template <int WK, int WP, int FK, int FP, int R, int S, int NS, int HJ, int PW, int CPS, int AL>
 __global__ void __launch_bounds__(64 * WK * WP)
 conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ w,
                        int8_t *__restrict__ y, I8Params p) {
-  using T = HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS>;
+  using T = HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL>;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
 
   const int tid = threadIdx.x;
@@ -405,6 +422,17 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
 
   const int NST = CB / CPS;  // stages (the plan keeps CB a multiple of CPS)
 
+  // AL = 1: the stage's filter follows its CPS halos; this wave's filter
+  // DMA j carries block g = j*NWAVES + wave = t*KB + kb of the stage.
+  const int filt_off = CPS * p.halo_bytes;
+  uint32_t fv_off[T::FJ > 0 ? T::FJ : 1];
+#pragma unroll
+  for (int j = 0; j < T::FJ; ++j) {
+    const int g = j * T::NWAVES + wave;
+    const int k = k0 + 32 * (g % T::KB) + l32;
+    fv_off[j] = g < T::FBLK && k < p.K ? (uint32_t)(k * 32 + 16 * half) : OOB_OFFSET;
+  }
+
   auto issue_stage = [&](int st) {
     unsigned char *base = lds + (st % NS) * p.stage_bytes;
     const bool live = st < NST;
@@ -415,6 +443,32 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
         unsigned char *dst = hv_dst[j] >= 0 ? base + c * p.halo_bytes + hv_dst[j] : dummy;
         lds_dma16(xr, dst, live ? hv_off[j] : OOB_OFFSET, live ? (st * CPS + c) * HW32 : 0);
       }
+#pragma unroll
+    for (int j = 0; j < T::FJ; ++j) {
+      const int g = j * T::NWAVES + wave;
+      const int t = g / T::KB;
+      const bool ok = g < T::FBLK;
+      lds_dma16(wr, ok ? base + filt_off + g * 1024 : dummy, live ? fv_off[j] : OOB_OFFSET,
+                live && ok ? (st * T::TPS + t) * KB32 : 0);
+    }
+  };
+
+  // AL = 1: the d-th of the NB DMAs of stage st (halo blocks, then filter)
+  auto issue_dma = [&](int st, int d) {
+    unsigned char *base = lds + (st % NS) * p.stage_bytes;
+    const bool live = st < NST;
+    if (d < HJ * CPS) {
+      const int c = d / HJ, j = d % HJ;
+      unsigned char *dst = hv_dst[j] >= 0 ? base + c * p.halo_bytes + hv_dst[j] : dummy;
+      lds_dma16(xr, dst, live ? hv_off[j] : OOB_OFFSET, live ? (st * CPS + c) * HW32 : 0);
+    } else {
+      const int j = d - HJ * CPS;
+      const int g = j * T::NWAVES + wave;
+      const int t = g / T::KB;
+      const bool ok = g < T::FBLK;
+      lds_dma16(wr, ok ? base + filt_off + g * 1024 : dummy, live ? fv_off[j] : OOB_OFFSET,
+                live && ok ? (st * T::TPS + t) * KB32 : 0);
+    }
   };
 
   // Filter fragments of global tap g = cb*RS + t into a register slot; taps
@@ -424,6 +478,14 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
     const int soff = (g < ntaps ? g : ntaps - 1) * KB32;
 #pragma unroll
     for (int i = 0; i < FK; ++i) dst[i] = load_b128_s(wr, a_off[i], soff);
+  };
+
+  v4i af[2][FK];
+  auto read_a = [&](int st, int t, v4i (&a)[FK]) {  // AL = 1; t: tap within the stage
+    const unsigned char *base = lds + (st % NS) * p.stage_bytes + filt_off;
+#pragma unroll
+    for (int i = 0; i < FK; ++i)
+      a[i] = *reinterpret_cast<const v4i *>(base + ((t * T::KB + wk * FK + i) * 64 + lane) * 16);
   };
 
   v4i bf[2][FP];
@@ -447,7 +509,7 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
   issue_stage(0);
   unsigned char *apro = lds + p.pro_off;
 #pragma unroll
-  for (int j = 0; j < T::AJ; ++j) {
+  for (int j = 0; j < T::AJ; ++j) {  // AL = 0 only (AJ = 0 otherwise)
     const int g = j * T::NWAVES + wave;
     const int tap = g / T::KB;
     const int kb = g - tap * T::KB;
@@ -462,11 +524,15 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
 #pragma unroll
   for (int s0 = 1; s0 < NS - 1; ++s0) issue_stage(s0);
   __builtin_amdgcn_sched_barrier(0);
+  if constexpr (AL) {
+    read_a(0, 0, af[0]);
+  } else {
 #pragma unroll
-  for (int g = 0; g < T::AHEAD; ++g)
+    for (int g = 0; g < T::AHEAD; ++g)
 #pragma unroll
-    for (int i = 0; i < FK; ++i)
-      aring[g][i] = *reinterpret_cast<const v4i *>(apro + ((g * T::KB + wk * FK + i) * 64 + lane) * 16);
+      for (int i = 0; i < FK; ++i)
+        aring[g][i] = *reinterpret_cast<const v4i *>(apro + ((g * T::KB + wk * FK + i) * 64 + lane) * 16);
+  }
   read_b(0, 0, bf[0]);
 
   auto stage = [&](auto par_c, int st) {
@@ -475,15 +541,26 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
     for (int t = 0; t < T::TPS; ++t) {
       const int cur = (t + PAR) & 1;
       const int nxt = (t + 1 + PAR) & 1;
-      load_a(st * T::TPS + t + T::AHEAD, aring[(t + T::AHEAD) % T::RS]);
+      if constexpr (!AL) load_a(st * T::TPS + t + T::AHEAD, aring[(t + T::AHEAD) % T::RS]);
+      if constexpr (AL) {
+        // this tap's share of stage st+NS-1's DMAs (the rest at the last tap)
+        if (t + 1 < T::TPS) {
+          if (t < T::NB) issue_dma(st + NS - 1, t);
+        } else {
+#pragma unroll
+          for (int d = T::TPS - 1; d < T::NB; ++d) issue_dma(st + NS - 1, d);
+        }
+      }
       if (t + 1 < T::TPS) {
+        if constexpr (AL) read_a(st, t + 1, af[nxt]);
         read_b(st, t + 1, bf[nxt]);
       } else {
         __builtin_amdgcn_sched_barrier(0);
         halo_wait<T::WAITL>();
         halo_barrier();
-        issue_stage(st + NS - 1);
+        if constexpr (!AL) issue_stage(st + NS - 1);
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (AL) read_a(st + 1, 0, af[nxt]);
         read_b(st + 1, 0, bf[nxt]);
       }
       // Pixel-fragment-major order: fragment b of this tap is done after its
@@ -493,13 +570,19 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
       for (int b = 0; b < FP; ++b)
 #pragma unroll
         for (int a = 0; a < FK; ++a)
-          acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(aring[t % T::RS][a], bf[cur][b],
-                                                            acc[a][b], 0, 0, 0);
+          acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(AL ? af[cur][a] : aring[t % T::RS][a],
+                                                            bf[cur][b], acc[a][b], 0, 0, 0);
 #pragma unroll
       for (int b = 0; b < FP; ++b) {
         __builtin_amdgcn_sched_group_barrier(0x008, FK, 0);  // fragment b's MFMAs
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
-        if (b < FK) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one filter load
+        if constexpr (AL) {
+          // this tap's reads for the next: FP pixel and FK filter fragments
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          if (b < FK) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        } else {
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+          if (b < FK) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one filter load
+        }
       }
     }
   };
@@ -528,19 +611,23 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
     // stage's wait; the ring holds the filter of its taps 0..RS-2 and the
     // last tap's is loaded here.
     const int st = NST - 1;
-    load_a(st * T::TPS + T::AHEAD, aring[T::AHEAD % T::RS]);
+    if constexpr (!AL) load_a(st * T::TPS + T::AHEAD, aring[T::AHEAD % T::RS]);
     const unsigned char *base = lds + (st % NS) * p.stage_bytes;
 #pragma unroll
     for (int b = 0; b < FP; ++b) {
-      v4i bb[2];
+      v4i bb[2], aa[2][FK];
       bb[0] = *reinterpret_cast<const v4i *>(base + b_addr_c[0][b] + tap_off[0]);
+      if constexpr (AL) read_a(st, 0, aa[0]);
 #pragma unroll
       for (int t = 0; t < T::RS; ++t) {
-        if (t + 1 < T::RS)
+        if (t + 1 < T::RS) {
           bb[(t + 1) & 1] = *reinterpret_cast<const v4i *>(base + b_addr_c[0][b] + tap_off[t + 1]);
+          if constexpr (AL) read_a(st, t + 1, aa[(t + 1) & 1]);
+        }
 #pragma unroll
         for (int a = 0; a < FK; ++a)
-          acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(aring[t][a], bb[t & 1], acc[a][b], 0, 0, 0);
+          acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(AL ? aa[t & 1][a] : aring[t][a], bb[t & 1],
+                                                            acc[a][b], 0, 0, 0);
       }
 #pragma unroll
       for (int a = 0; a < FK; ++a) store_i8_frag(acc[a][b], y, p, m_wave + 32 * b, kb_wave + a, lane);
@@ -552,15 +639,15 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
   }
 }
 
-template <int WK, int WP, int FK, int FP, int R, int S, int NS, int HJ, int PW, int CPS>
+template <int WK, int WP, int FK, int FP, int R, int S, int NS, int HJ, int PW, int CPS, int AL>
 static hipError_t launch_i8_halo_ad(const int8_t *x, const int8_t *w, int8_t *y,
                                     const I8Params &p, int grid, hipStream_t s) {
-  using T = HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS>;
+  using T = HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL>;
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void *>(&conv_i8_halo_ad_kernel<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS>),
+      reinterpret_cast<const void *>(&conv_i8_halo_ad_kernel<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL>),
       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((conv_i8_halo_ad_kernel<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS>), dim3(grid),
+  hipLaunchKernelGGL((conv_i8_halo_ad_kernel<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL>), dim3(grid),
                      dim3(T::THREADS), p.lds_bytes, s, x, w, y, p);
   return hipGetLastError();
 }
@@ -586,16 +673,20 @@ static hipError_t launch_i8_halo(const int8_t *x, const int8_t *w, int8_t *y,
         &launch_i8_halo<WK, WP, FK, FP, R, S, NS, HJ>, 1, R, S, WK * WP, NS, HJ        \
   }
 
-#define I8_HALO_AD_CFG(WK, WP, FK, FP, R, S, NS, HJ, PW, CPS)                         \
+#define I8_HALO_AD_CFG_X(KINDNAME, WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL)          \
   I8Config {                                                                          \
-    "i8_halo_regfilter_mfma32x32x32_wg" #WK "x" #WP "_frag" #FK "x" #FP "_r" #R "s" #S    \
+    "i8_halo_" KINDNAME "_mfma32x32x32_wg" #WK "x" #WP "_frag" #FK "x" #FP "_r" #R "s" #S \
     "_ring" #NS "_hj" #HJ "_pitch" #PW "_cps" #CPS,                                     \
-        HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS>::BM,                          \
-        HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS>::BN,                          \
-        HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS>::THREADS, 0, R * S, 0,        \
-        &launch_i8_halo_ad<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS>, 2, R, S, WK * WP, NS, HJ, \
-        PW, CPS                                                                       \
+        HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL>::BM,                      \
+        HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL>::BN,                      \
+        HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL>::THREADS, 0, R * S, 0,    \
+        &launch_i8_halo_ad<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL>, 2, R, S, WK * WP, NS, \
+        HJ, PW, CPS, AL                                                               \
   }
+#define I8_HALO_AD_CFG(WK, WP, FK, FP, R, S, NS, HJ, PW, CPS) \
+  I8_HALO_AD_CFG_X("regfilter", WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, 0)
+#define I8_HALO_LF_CFG(WK, WP, FK, FP, R, S, NS, HJ, PW, CPS) \
+  I8_HALO_AD_CFG_X("ldsfilter", WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, 1)
 
 I8Config kI8HaloConfigs[] = {
     I8_HALO_CFG(2, 4, 2, 2, 3, 3, 3, 4),  // 128 ch x 256 px, 8 waves of 64x64
@@ -628,6 +719,9 @@ I8Config kI8HaloConfigs[] = {
     I8_HALO_AD_CFG(2, 4, 2, 2, 3, 3, 3, 2, 32, 2),
     I8_HALO_AD_CFG(2, 4, 2, 2, 3, 3, 4, 2, 32, 2),
     I8_HALO_AD_CFG(2, 2, 2, 4, 3, 3, 3, 4, 32, 2),
+    // filter in the LDS ring as well, fetched once per workgroup
+    I8_HALO_LF_CFG(2, 4, 2, 2, 3, 3, 3, 2, 32, 1),   // 8 waves of 64x64
+    I8_HALO_LF_CFG(2, 2, 2, 4, 3, 3, 3, 4, 32, 1),   // 4 waves of 64x128
 };
 int kNumI8HaloConfigs = sizeof(kI8HaloConfigs) / sizeof(kI8HaloConfigs[0]);
 

@@ -51,6 +51,7 @@ struct I8Config {
   int fr, fs, nwaves, ns, hj;
   int pw;   // kind 2: halo row pitch in LDS (0: the halo width; > 0: fixed, dilation 1)
   int cps;  // kind 2: channel blocks per ring stage (C/32 must be a multiple)
+  int al;   // kind 2: 1 = filter taps in the LDS ring too, 0 = in registers
 };
 
 // Host-only tables (not const: a const namespace-scope object would also be

@@ -1,0 +1,249 @@
+"""Configuration sweep for one conv2d fprop shape.
+
+Runs every compiled configuration that can run the shape, back to back on
+one stream, and reports each one's device time; the configuration the
+library picks by itself for the shape is marked.  This is the evidence
+behind the per-shape table in api.hip (kShapeTable).
+
+    python -m convolution_forward_gemm_amd.sweep --workload c3
+
+Under `rocprofv3 --kernel-trace` the same run gives each configuration's
+dispatch durations; `--summarize-trace DIR` turns that output into a table
+under profiles/ (each configuration runs a kernel instantiation of its own,
+and the sweep runs them in configuration order, so a kernel name maps to the
+configuration that first dispatched it).  With `--graph` each configuration
+is also timed per call in HIP-graph replay (20 captured back-to-back calls),
+the criterion for the launch-latency-bound shapes; `--sweep-log FILE` adds
+that table, from the sweep's own JSON line, to the summary.
+
+Inputs are the seeded synthetic operands of the workload, already resident
+in device memory; the GPU first runs the default configuration long enough
+to reach its steady clock.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import json
+import os
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+
+
+def _ops(wk, P, Q):
+    return 2 * wk.N * wk.K * P * Q * wk.C * wk.R * wk.S
+
+
+def _new_conv(b, wk):
+    return b.Conv2dFprop(wk.N, wk.C, wk.H, wk.W, wk.K, wk.R, wk.S, pad=wk.pad,
+                         stride=wk.stride, dil=wk.dil, dtype=wk.dtype)
+
+
+def applicable(b, wk):
+    """[(index, config string)] of the configurations that run the shape, and
+    the index the library chooses by itself."""
+    conv = _new_conv(b, wk)
+    default = int(conv.config.split()[0].split("=")[1])
+    out = []
+    for i in range(b.num_configs(wk.dtype)):
+        try:
+            conv.set_config(i)
+        except b.ConvError as e:
+            if e.status != b.CONV_ERR_UNSUPPORTED:
+                raise
+            continue
+        out.append((i, conv.config))
+    return out, default
+
+
+def _graph_us(torch, conv, xp, wp, yp, alpha, reps=30):
+    """Median microseconds per call over replays of 20 captured calls."""
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        for _ in range(3):
+            conv.run_ptr(xp, wp, yp, alpha, s.cuda_stream)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for _ in range(20):
+            conv.run_ptr(xp, wp, yp, alpha, s.cuda_stream)
+    t = []
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        t.append(e0.elapsed_time(e1) * 1e3 / 200)
+    t.sort()
+    return t[len(t) // 2]
+
+
+def run_sweep(key, calls, warmup, rounds, graph=False):
+    import torch
+    from . import binding as b
+    from . import workloads as wl
+
+    wk = wl.WORKLOADS[key]
+    cfgs, default = applicable(b, wk)
+    x, w = wl.make_inputs(wk)
+    if wk.dtype == "int8":
+        xd = b.nchw_to_nc32hw32(torch.from_numpy(x).cuda())
+        wd = b.kcrs_to_c32rsk32(torch.from_numpy(w).cuda())
+        ydt = torch.int8
+    else:
+        xd, wd = torch.from_numpy(x).cuda(), torch.from_numpy(w).cuda()
+        ydt = torch.float32
+    convs = []
+    for i, _ in cfgs:
+        c = _new_conv(b, wk)
+        c.set_config(i)
+        convs.append(c)
+    y = torch.empty(convs[0].y_shape, dtype=ydt, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    xp, wp, yp = xd.data_ptr(), wd.data_ptr(), y.data_ptr()
+    # steady clock first (default configuration), then every configuration
+    # once in index order (this fixes the kernel-name order in a trace)
+    dflt = convs[[i for i, _ in cfgs].index(default)]
+    for _ in range(warmup):
+        dflt.run_ptr(xp, wp, yp, wk.alpha, s)
+    for c in convs:
+        c.run_ptr(xp, wp, yp, wk.alpha, s)
+    torch.cuda.synchronize()
+    times = {i: [] for i, _ in cfgs}
+    for _ in range(rounds):
+        for (i, _), c in zip(cfgs, convs):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(calls):
+                c.run_ptr(xp, wp, yp, wk.alpha, s)
+            e1.record()
+            torch.cuda.synchronize()
+            times[i].append(e0.elapsed_time(e1) * 1e3 / calls)
+    gus = {}
+    if graph:
+        for (i, _), c in zip(cfgs, convs):
+            gus[i] = _graph_us(torch, c, xp, wp, yp, wk.alpha)
+    ops = _ops(wk, convs[0].P, convs[0].Q)
+    rows = []
+    for i, cfg in cfgs:
+        t = sorted(times[i])
+        med = t[len(t) // 2]
+        rows.append({"config": i, "name": cfg.split()[1], "us": round(med, 3),
+                     "tops": round(ops / med / 1e6, 1), "default": i == default})
+        if graph:
+            rows[-1]["graph_us"] = round(gus[i], 3)
+    return {"workload": key, "name": wk.name, "calls": calls, "rounds": rounds,
+            "warmup": warmup, "rows": rows}
+
+
+def _find(d, suffix):
+    hits = sorted(glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True))
+    if not hits:
+        raise FileNotFoundError("no *%s under %s" % (suffix, d))
+    return hits[0]
+
+
+def summarize_trace(key, trace_dir, command, out_dir, sweep_log=None):
+    """profiles/conv_config_sweep_<key>.txt from a rocprofv3 --kernel-trace
+    run of this sweep (and, given its log, the graph-replay table)."""
+    from . import binding as b
+    from . import workloads as wl
+
+    wk = wl.WORKLOADS[key]
+    cfgs, default = applicable(b, wk)
+    with open(_find(trace_dir, "kernel_trace.csv")) as f:
+        rows = sorted(csv.DictReader(f), key=lambda r: int(r["Start_Timestamp"]))
+    conv_rows = [r for r in rows if "conv_" in r["Kernel_Name"] and "_to_" not in r["Kernel_Name"]]
+    durs, order = {}, []
+    for r in conv_rows:
+        k = r["Kernel_Name"]
+        durs.setdefault(k, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+        if k not in order:
+            order.append(k)
+    # the warm-up runs the default configuration first; then every
+    # configuration once in index order
+    first = order[0]
+    seq = [k for k in order if k != first]
+    idx = [i for i, _ in cfgs]
+    mapping = {}
+    pos = idx.index(default)
+    rest = idx[:pos] + idx[pos + 1:]
+    if len(seq) != len(rest):
+        raise ValueError("%d kernels for %d configurations: a kernel runs two of them"
+                         % (len(seq) + 1, len(idx)))
+    mapping[first] = default
+    for k, i in zip(seq, rest):
+        mapping[k] = i
+    conv = _new_conv(b, wk)
+    ops = _ops(wk, conv.P, conv.Q)
+    cname = dict(cfgs)
+    lines = ["rocprofv3 kernel-trace sweep of every configuration that runs: " + wk.name,
+             "command: " + command,
+             "(each configuration's dispatch durations; the warm-up dispatches of the "
+             "default configuration are excluded)", "",
+             "%-4s %-92s %6s %10s %10s %9s" % ("cfg", "configuration", "calls", "avg_us", "min_us", "TOPS")]
+    res = []
+    for k, i in mapping.items():
+        d = durs[k]
+        if i == default:
+            d = d[-(len(durs[seq[0]]) if seq else len(d)):]  # drop the warm-up
+        avg = sum(d) / len(d) / 1e3
+        res.append((avg, i, len(d), min(d) / 1e3))
+    for avg, i, n, mn in sorted(res):
+        unit = ops / avg / 1e6
+        lines.append("%-4d %-92s %6d %10.2f %10.2f %9.1f%s" % (
+            i, cname[i].split()[1][:92], n, avg, mn, unit, "  <- chosen" if i == default else ""))
+    best = min(res)
+    tail = ["", "chosen configuration %d; fastest by trace average: %d (%.2f us)" % (default, best[1], best[0])]
+    if sweep_log:
+        with open(sweep_log) as f:
+            js = [json.loads(l) for l in f if l.startswith("{")][-1]
+        g = sorted((r["graph_us"], r["config"]) for r in js["rows"] if "graph_us" in r)
+        if g:
+            lines += ["", "graph replay (20 captured back-to-back calls, same run), us per call:",
+                      "%-4s %-92s %10s" % ("cfg", "configuration", "us/call")]
+            for us, i in g:
+                lines.append("%-4d %-92s %10.3f%s" % (i, cname[i].split()[1][:92], us,
+                                                       "  <- chosen" if i == default else ""))
+            tail.append("fastest per call in graph replay: %d (%.3f us)" % (g[0][1], g[0][0]))
+    lines += tail
+    path = os.path.join(out_dir, "conv_config_sweep_%s.txt" % key)
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return path
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--workload", default="c3")
+    ap.add_argument("--calls", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=3000)
+    ap.add_argument("--rounds", type=int, default=3)
+    ap.add_argument("--graph", action="store_true", help="also time each configuration in graph replay")
+    ap.add_argument("--summarize-trace", metavar="DIR")
+    ap.add_argument("--sweep-log", metavar="FILE", help="with --summarize-trace: the sweep's output")
+    ap.add_argument("--command", default="")
+    ap.add_argument("--out-dir", default=os.path.join(ROOT, "profiles"))
+    a = ap.parse_args()
+    if a.summarize_trace:
+        print(summarize_trace(a.workload, a.summarize_trace, a.command, a.out_dir, a.sweep_log))
+        return
+    res = run_sweep(a.workload, a.calls, a.warmup, a.rounds, a.graph)
+    for r in sorted(res["rows"], key=lambda r: r["us"]):
+        print("%3d %-90s %9.2f us %8.1f %s" % (r["config"], r["name"], r["us"], r["tops"],
+                                               "<- chosen" if r["default"] else ""), flush=True)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    if __package__ in (None, ""):
+        sys.path.insert(0, ROOT)
+        __package__ = "convolution_forward_gemm_amd"
+    main()

@@ -122,9 +122,11 @@ def test_register_filter_kernels_ring_waits(halo_asm):
     fns = _functions(halo_asm, "_ZN9convfprop22conv_i8_halo_ad_kernel")
     assert len(fns) >= 3
     for name, body in fns.items():
-        wk, wp, fk, _, r, s, ns = _template_ints(name)[:7]  # <WK, WP, FK, FP, R, S, NS, HJ, ...>
-        # the prologue's filter taps 0..R*S-2: (R*S-1)*WK*FK blocks over WK*WP waves
-        aj = ((r * s - 1) * wk * fk + wk * wp - 1) // (wk * wp)
+        ints = _template_ints(name)  # <WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL>
+        wk, wp, fk, _, r, s, ns = ints[:7]
+        # the prologue's filter taps 0..R*S-2: (R*S-1)*WK*FK blocks over WK*WP
+        # waves; with the filter in the LDS ring (AL) they are part of stage 0
+        aj = 0 if ints[10] else ((r * s - 1) * wk * fk + wk * wp - 1) // (wk * wp)
         _check_kernel(name, body, ns, aj)
 
 

@@ -469,7 +469,7 @@ def main():
         # fp32 dilated
         w5 = wl.WORKLOADS["c5"]
         c5, x5, w5d, y5, _ = setup(w5, torch, b)
-        ms5 = time_device(torch, lambda: c5.run_ptr(x5.data_ptr(), w5d.data_ptr(), y5.data_ptr(), 1.0, s4), 10, 2)
+        ms5 = time_device(torch, lambda: c5.run_ptr(x5.data_ptr(), w5d.data_ptr(), y5.data_ptr(), 1.0, s4), 20, 15)
         t5 = conv_ops(w5, c5.P, c5.Q) / (ms5 * 1e-3) / 1e12
         extra["c5_fp32_dilated"] = {"ms": round(ms5, 4), "TFLOPS": round(t5, 3),
                                     "pct_of_fp32_peak": round(100 * t5 / PEAK_FP32_TFLOPS, 2),

@@ -98,10 +98,11 @@ const ShapeEntry kShapeTable[] = {
     // halo row pitch and a 3-stage ring
     {CONV_DTYPE_INT8, 32, 128, 56, 56, 256, 3, 3, 1, 1, 2, 2, 1, 1,
      "i8_halo_regfilter_mfma32x32x32_wg2x4_frag2x2_r3s3_ring3_hj6_pitch64_cps1"},
-    // fp32 5x9 dilated N8 C32 512x512 K64: 8 waves, 64 ch x 512 px per
-    // workgroup (half the weight staging per pixel of a 4-wave tile)
+    // fp32 5x9 dilated N8 C32 512x512 K64: 16 waves, 64 ch x 1024 px per
+    // workgroup (a quarter of a 4-wave tile's weight staging per pixel),
+    // the next channel chunk's weights staged while the current one runs
     {CONV_DTYPE_FP32, 8, 32, 512, 512, 64, 5, 9, 2, 4, 1, 1, 2, 3,
-     "f32_mfma32x32x2_8waves_frag2x2_cc4_depth3"},
+     "f32_mfma32x32x2_16waves_frag2x2_cc4_depth3_dbuf"},
 };
 
 int lookup_shape(const conv2d_fprop_desc_s &d) {
@@ -232,6 +233,7 @@ bool plan(conv2d_fprop_desc_s &d, int cfg) {
     if (cfg < 0 || cfg >= kNumF32Configs) return false;
     const F32Config &c = kF32Configs[cfg];
     if (f32_lds_bytes(d, cfg) > 160 * 1024) return false;
+    if (c.max_rs > 0 && d.R * d.S > c.max_rs) return false;
     const int64_t mt = (M + c.bn - 1) / c.bn, kt = (d.K + c.bm - 1) / c.bm;
     if (mt * kt > 0x7fffffff) return false;
     F32Params &p = d.f32;

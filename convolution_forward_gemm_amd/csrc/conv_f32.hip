@@ -19,7 +19,11 @@
 //   * Weights of a channel chunk are staged once per workgroup into LDS,
 //     transposed to [c][r][s][k] (row pitch BM+1) so that an MFMA operand is
 //     32 consecutive floats (conflict-free ds_read_b32); the staging reads
-//     each output channel's contiguous run of the chunk with whole waves.  The activation operand is read
+//     each output channel's contiguous run of the chunk with whole waves.
+//     With DB = 1 the staging is double-buffered: the next chunk's weights
+//     are loaded into registers at the start of a chunk, written to the
+//     other LDS buffer at its end, and one barrier per chunk separates the
+//     two (CC*R*S <= 64*MAXJ).  The activation operand is read
 //     straight from global memory (L1/L2 serve the R*S-fold reuse), with a
 //     software pipeline of DEPTH taps in flight.
 #include "common.hpp"
@@ -27,7 +31,7 @@
 
 namespace convfprop {
 
-template <int FK, int FP, int CC, int DEPTH, int NW = 4>
+template <int FK, int FP, int CC, int DEPTH, int NW = 4, int DB = 0>
 struct F32Tile {
   static constexpr int NWAVES = NW;
   static constexpr int THREADS = 64 * NW;
@@ -35,15 +39,18 @@ struct F32Tile {
   static constexpr int BN = 32 * FP * NWAVES;  // output pixels per workgroup
   static constexpr int PAIRS = CC / 2;         // MFMAs per tap per fragment
   static constexpr int LDP = BM + 1;           // LDS row pitch of the staged weights
+  static constexpr int ROWS = THREADS / 64;    // output channels per staging pass
+  static constexpr int KI = BM / ROWS;         // staging passes per 64-weight segment
+  static constexpr int MAXJ = 4;               // DB: 64-weight segments held in registers
   static_assert(CC % 2 == 0, "channel chunk must hold whole pairs");
   static_assert(THREADS % 64 == 0 && BM % (THREADS / 64) == 0, "staging rows per pass");
 };
 
-template <int FK, int FP, int CC, int DEPTH, int NW>
+template <int FK, int FP, int CC, int DEPTH, int NW, int DB>
 __global__ void __launch_bounds__(64 * NW)
 conv_f32_kernel(const float *__restrict__ x, const float *__restrict__ w,
                 float *__restrict__ y, F32Params p) {
-  using T = F32Tile<FK, FP, CC, DEPTH, NW>;
+  using T = F32Tile<FK, FP, CC, DEPTH, NW, DB>;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
   float *wl = reinterpret_cast<float *>(lds_raw);  // [CC][R][S][LDP]
 
@@ -91,14 +98,51 @@ conv_f32_kernel(const float *__restrict__ x, const float *__restrict__ w,
   const int crs = CC * RS;  // weights of one output channel in a chunk
   const float alpha = p.alpha;
 
-  for (int c0 = 0; c0 < p.C; c0 += CC) {
+  // DB: the next chunk's weights, thread (jl, kr) holding W[k0 + kr + ki*ROWS]
+  // [c0 ..)[j = ji*64 + jl] (the same element-to-thread map as the staging
+  // loop below), and the LDS buffer the current chunk reads.
+  float wnext[DB ? T::MAXJ : 1][DB ? T::KI : 1];
+  auto wload = [&](int c0n) {
+    const int jl = tid & 63;
+    const int kr = tid >> 6;
+#pragma unroll
+    for (int ji = 0; ji < (DB ? T::MAXJ : 1); ++ji) {
+      const int j = ji * 64 + jl;
+      const int c = c0n + j / RS;
+#pragma unroll
+      for (int ki = 0; ki < (DB ? T::KI : 1); ++ki) {
+        const int k = k0 + kr + ki * T::ROWS;
+        wnext[ji][ki] = (j < crs && k < p.K && c < p.C) ? w[((size_t)k * p.C + c0n) * RS + j] : 0.0f;
+      }
+    }
+  };
+  auto wstore = [&](float *buf) {
+    const int jl = tid & 63;
+    const int kr = tid >> 6;
+#pragma unroll
+    for (int ji = 0; ji < (DB ? T::MAXJ : 1); ++ji) {
+      const int j = ji * 64 + jl;
+      if (j < crs) {
+#pragma unroll
+        for (int ki = 0; ki < (DB ? T::KI : 1); ++ki) buf[j * T::LDP + kr + ki * T::ROWS] = wnext[ji][ki];
+      }
+    }
+  };
+  if constexpr (DB) {
+    wload(0);
+    wstore(wl);
+    __syncthreads();
+  }
+
+  for (int c0 = 0, chunk = 0; c0 < p.C; c0 += CC, ++chunk) {
+    float *wcur = wl + (DB ? (chunk & 1) * crs * T::LDP : 0);
     // ---- stage W[k0 .. k0+BM)[c0 .. c0+CC)[r][s] into LDS as [cc][r][s][k].
     // For one output channel the chunk's CC*R*S weights are contiguous in
     // global memory: a wave reads 64 consecutive of them (one row segment)
     // and writes them down an LDS column; the odd row pitch BM+1 keeps
     // those writes on 64 different banks.  No division per element.
+    if constexpr (!DB) {
     __syncthreads();
-    {
       constexpr int ROWS = T::THREADS / 64;  // output channels per pass
       const int jl = tid & 63;
       const int kr = tid >> 6;
@@ -113,8 +157,8 @@ conv_f32_kernel(const float *__restrict__ x, const float *__restrict__ w,
           if (j < crs) wl[j * T::LDP + kk] = v;
         }
       }
-    }
     __syncthreads();
+    }
 
     // ---- taps of this chunk, software-pipelined DEPTH deep ---------------
     // For each tap a lane loads T::PAIRS values per pixel fragment: channel
@@ -155,6 +199,10 @@ conv_f32_kernel(const float *__restrict__ x, const float *__restrict__ w,
 
 #pragma unroll
     for (int d = 0; d < DEPTH - 1; ++d) load_next(ring[d]);
+    // DB: the next chunk's weights go out behind the first activation taps,
+    // a whole chunk ahead of their use
+    const bool has_next = c0 + CC < p.C;
+    if (DB && has_next) wload(c0 + CC);
 
     const int rs_blocks = (RS + DEPTH - 1) / DEPTH;
     for (int blk = 0; blk < rs_blocks; ++blk) {
@@ -172,7 +220,7 @@ conv_f32_kernel(const float *__restrict__ x, const float *__restrict__ w,
           float af[FK];
 #pragma unroll
           for (int a = 0; a < FK; ++a)
-            af[a] = wl[((2 * i + half) * RS + ttw) * T::LDP + 32 * a + l32];
+            af[a] = wcur[((2 * i + half) * RS + ttw) * T::LDP + 32 * a + l32];
 #pragma unroll
           for (int a = 0; a < FK; ++a)
 #pragma unroll
@@ -181,6 +229,12 @@ conv_f32_kernel(const float *__restrict__ x, const float *__restrict__ w,
                                                                acc[a][b], 0, 0, 0);
         }
       }
+    }
+    if constexpr (DB) {
+      // the other buffer was last read in the previous chunk, before the
+      // barrier that ended it
+      if (has_next) wstore(wl + ((chunk + 1) & 1) * crs * T::LDP);
+      __syncthreads();
     }
   }
 
@@ -203,33 +257,38 @@ conv_f32_kernel(const float *__restrict__ x, const float *__restrict__ w,
   }
 }
 
-template <int FK, int FP, int CC, int DEPTH, int NW>
+template <int FK, int FP, int CC, int DEPTH, int NW, int DB>
 static hipError_t launch_f32(const float *x, const float *w, float *y,
                              const F32Params &p, int grid, hipStream_t s) {
-  using T = F32Tile<FK, FP, CC, DEPTH, NW>;
-  const int lds = CC * p.R * p.S * T::LDP * 4;
+  using T = F32Tile<FK, FP, CC, DEPTH, NW, DB>;
+  const int lds = CC * p.R * p.S * T::LDP * 4 * (DB ? 2 : 1);
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void *>(&conv_f32_kernel<FK, FP, CC, DEPTH, NW>),
+      reinterpret_cast<const void *>(&conv_f32_kernel<FK, FP, CC, DEPTH, NW, DB>),
       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((conv_f32_kernel<FK, FP, CC, DEPTH, NW>), dim3(grid),
+  hipLaunchKernelGGL((conv_f32_kernel<FK, FP, CC, DEPTH, NW, DB>), dim3(grid),
                      dim3(T::THREADS), lds, s, x, w, y, p);
   return hipGetLastError();
 }
 
-#define F32_CFG_W(FK, FP, CC, DEPTH, NW, NAME)                                       \
+#define F32_CFG_W(FK, FP, CC, DEPTH, NW, DB, NAME)                                   \
   F32Config {                                                                        \
-    NAME, F32Tile<FK, FP, CC, DEPTH, NW>::BM, F32Tile<FK, FP, CC, DEPTH, NW>::BN, 64 * NW,  \
-        CC * 4 * F32Tile<FK, FP, CC, DEPTH, NW>::LDP, 0, &launch_f32<FK, FP, CC, DEPTH, NW> \
+    NAME, F32Tile<FK, FP, CC, DEPTH, NW, DB>::BM, F32Tile<FK, FP, CC, DEPTH, NW, DB>::BN, \
+        64 * NW, CC * 4 * F32Tile<FK, FP, CC, DEPTH, NW, DB>::LDP * (DB ? 2 : 1),      \
+        DB ? 64 * F32Tile<FK, FP, CC, DEPTH, NW, DB>::MAXJ / CC : 0,                  \
+        &launch_f32<FK, FP, CC, DEPTH, NW, DB>                                         \
   }
 #define F32_CFG(FK, FP, CC, DEPTH) \
-  F32_CFG_W(FK, FP, CC, DEPTH, 4, "f32_mfma32x32x2_frag" #FK "x" #FP "_cc" #CC "_depth" #DEPTH)
+  F32_CFG_W(FK, FP, CC, DEPTH, 4, 0, "f32_mfma32x32x2_frag" #FK "x" #FP "_cc" #CC "_depth" #DEPTH)
 #define F32_CFG16(FK, FP, CC, DEPTH) \
-  F32_CFG_W(FK, FP, CC, DEPTH, 16,   \
+  F32_CFG_W(FK, FP, CC, DEPTH, 16, 0, \
             "f32_mfma32x32x2_16waves_frag" #FK "x" #FP "_cc" #CC "_depth" #DEPTH)
 #define F32_CFG8(FK, FP, CC, DEPTH) \
-  F32_CFG_W(FK, FP, CC, DEPTH, 8,   \
+  F32_CFG_W(FK, FP, CC, DEPTH, 8, 0, \
             "f32_mfma32x32x2_8waves_frag" #FK "x" #FP "_cc" #CC "_depth" #DEPTH)
+#define F32_CFG16_DB(FK, FP, CC, DEPTH) \
+  F32_CFG_W(FK, FP, CC, DEPTH, 16, 1, \
+            "f32_mfma32x32x2_16waves_frag" #FK "x" #FP "_cc" #CC "_depth" #DEPTH "_dbuf")
 
 // lds_bytes here is per filter tap (times R*S at launch).
 F32Config kF32Configs[] = {
@@ -243,6 +302,11 @@ F32Config kF32Configs[] = {
     F32_CFG16(2, 2, 4, 3), // 7: 64 ch x 1024 px, 16 waves
     F32_CFG8(2, 2, 4, 5),  // 8: 8 waves, deeper activation prefetch
     F32_CFG8(2, 2, 8, 3),  // 9: 8 waves, 8-channel chunks
+    // 10: config 7 with double-buffered weight staging.  Its two weight
+    // buffers (94 KB at 5x9) leave room for one workgroup per CU, which with
+    // 16 waves keeps four per SIMD; an 8-wave workgroup with two buffers
+    // drops to two waves per SIMD and runs 7% slower than config 5.
+    F32_CFG16_DB(2, 2, 4, 3),
 };
 int kNumF32Configs = sizeof(kF32Configs) / sizeof(kF32Configs[0]);
 

@@ -80,7 +80,8 @@ typedef hipError_t (*F32LaunchFn)(const float *x, const float *w, float *y,
 struct F32Config {
   const char *name;
   int bm, bn, threads, lds_bytes;
-  int max_crs;  // largest C*R*S... 0 = unlimited
+  int max_rs;   // largest R*S it runs (double-buffered staging holds a chunk
+                // in registers), 0 = any
   F32LaunchFn launch;
 };
 

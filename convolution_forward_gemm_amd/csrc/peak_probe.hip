@@ -4,6 +4,7 @@
 // Every kernel touches only its own buffers, at in-bounds offsets.
 // Build: hipcc --offload-arch=gfx950 -O3 peak_probe.hip -o peak_probe
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdio.h>
 
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -130,6 +131,28 @@ __global__ void __launch_bounds__(256) mfma_f32(v16f *out, int iters) {
     c3 = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c3, 0, 0, 0);
   }
   out[blockIdx.x * 256 + threadIdx.x] = c0 + c1 + c2 + c3;
+}
+
+// fp32 MFMA with normally distributed operands that change from one MFMA to
+// the next (the fp32 workload's data), eight accumulator chains.
+__global__ void __launch_bounds__(256) mfma_f32_rand(const float *__restrict__ src, v16f *out, int iters) {
+  const int t = threadIdx.x;
+  float a[4], b[4];
+  for (int k = 0; k < 4; ++k) {
+    a[k] = src[(k * 256 + t) & 4095];
+    b[k] = src[((k + 4) * 256 + t) & 4095];
+  }
+  v16f c[8] = {};
+  for (int i = 0; i < iters; i += 4) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        c[j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[(j + u) & 3], b[((j >> 1) + u) & 3], c[j], 0, 0, 0);
+  }
+  v16f s = {};
+  for (int k = 0; k < 8; ++k) s += c[k];
+  out[blockIdx.x * 256 + t] = s;
 }
 
 // ds_read_b128 with lane-contiguous addresses (the conv kernels' pattern).
@@ -282,6 +305,36 @@ int main() {
   CHECK(hipEventElapsedTime(&ms, e0, e1));
   printf("fp32 MFMA v_mfma_f32_32x32x2_f32 : %8.1f TFLOPS\n",
          2.0 * 32 * 32 * 2 * 4 * (double)(iters / 4) * grid * 4 / ms / 1e9);
+
+  {
+    // normally distributed fp32 operands (Box-Muller on a fixed LCG stream)
+    float *rf;
+    CHECK(hipMalloc(&rf, 4096 * sizeof(float)));
+    static float host[4096];
+    unsigned st = 777u;
+    for (int i = 0; i < 4096; i += 2) {
+      st = st * 1664525u + 1013904223u;
+      const double u1 = ((st >> 8) + 1.0) / 16777217.0;
+      st = st * 1664525u + 1013904223u;
+      const double u2 = (st >> 8) / 16777216.0;
+      const double r = sqrt(-2.0 * log(u1));
+      host[i] = (float)(r * cos(6.283185307179586 * u2));
+      host[i + 1] = (float)(r * sin(6.283185307179586 * u2));
+    }
+    CHECK(hipMemcpy(rf, host, sizeof(host), hipMemcpyHostToDevice));
+    const int fit = iters / 4;  // a multiple of 4
+    hipLaunchKernelGGL(mfma_f32_rand, dim3(ncu), dim3(256), 0, 0, (const float *)rf, (v16f *)out, 100);
+    CHECK(hipDeviceSynchronize());
+    CHECK(hipEventRecord(e0));
+    for (int r = 0; r < 4; ++r)
+      hipLaunchKernelGGL(mfma_f32_rand, dim3(ncu), dim3(256), 0, 0, (const float *)rf, (v16f *)out, fit);
+    CHECK(hipEventRecord(e1));
+    CHECK(hipEventSynchronize(e1));
+    CHECK(hipEventElapsedTime(&ms, e0, e1));
+    printf("fp32 MFMA, N(0,1) operands, %3d CUs : %8.1f TFLOPS\n", ncu,
+           4 * 2.0 * 32 * 32 * 2 * 8 * (double)fit * ncu * 4 / ms / 1e9);
+    CHECK(hipFree(rf));
+  }
 
   for (int wgs = 1; wgs <= 2; ++wgs) {
     const int g = ncu * wgs;

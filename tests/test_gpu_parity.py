@@ -144,6 +144,8 @@ RAGGED = [
     (2, 256, 9, 7, 320, 3, 3, (1, 1), (1, 1), (1, 1)),     # C/32 = 8, ragged K tile
     (1, 128, 11, 10, 64, 3, 2, (1, 0), (2, 2), (2, 1)),    # C/32 = 4, stride and dilation
     (3, 256, 5, 6, 96, 1, 1, (0, 0), (1, 1), (1, 1)),      # 1x1, C/32 = 8
+    (3, 64, 23, 21, 96, 3, 3, (1, 1), (2, 2), (1, 1)),     # stride 2, ragged M and K tiles
+    (1, 64, 56, 56, 64, 3, 3, (1, 1), (2, 2), (1, 1)),     # stride 2, 57-column halo rows
 ]
 
 

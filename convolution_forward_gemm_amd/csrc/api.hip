@@ -217,6 +217,7 @@ bool plan(conv2d_fprop_desc_s &d, int cfg) {
     p.k_tiles = (int)kt;
     p.x_bytes = (uint32_t)d.x_bytes;
     p.w_bytes = (uint32_t)d.w_bytes;
+    p.y_bytes = (uint32_t)d.y_bytes;
     p.alpha = 1.0f;
     p.N = d.N;
     p.HV = p.WV = p.halo_dpp = p.halo_bytes = p.stage_bytes = 0;

@@ -404,6 +404,12 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
     }
     b_addr[i] = half * plane + a;
   }
+  // output offsets of this wave's pixel fragments (decoded here, off the
+  // epilogue's critical path)
+  const __amdgpu_buffer_rsrc_t yr = make_rsrc(y, p.y_bytes);
+  uint32_t y_off[FP];
+#pragma unroll
+  for (int i = 0; i < FP; ++i) y_off[i] = i8_pixel_yoff(p, m0 + 32 * (wp * FP + i) + l32, half);
   // the halo of the stage's c-th channel block sits c * halo_bytes further
   int b_addr_c[CPS][FP];
 #pragma unroll
@@ -630,7 +636,7 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
                                                             acc[a][b], 0, 0, 0);
       }
 #pragma unroll
-      for (int a = 0; a < FK; ++a) store_i8_frag(acc[a][b], y, p, m_wave + 32 * b, kb_wave + a, lane);
+      for (int a = 0; a < FK; ++a) store_i8_frag(acc[a][b], yr, y_off[b], kb_wave + a, p);
     }
     halo_wait<0>();  // no LDS-DMA (of the ring's idle stages) may outlive the workgroup
   } else {

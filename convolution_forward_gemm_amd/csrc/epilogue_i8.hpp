@@ -38,40 +38,42 @@ __device__ __forceinline__ uint32_t pack_low_bytes(uint32_t b0, uint32_t b1, uin
   return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
 }
 
-// Stores an FK x FP grid of 32x32 MFMA accumulator tiles (rows = output
-// channels, columns = output pixels) into y in NCxHWx<32> over K.
+// Byte offset in y (NCxHWx<32> over K) of output pixel m's first 32-channel
+// block, plus this lane half's 16 bytes; OOB_OFFSET for pixels past M, so
+// that their stores are dropped.  Adding kb * PQ * 32 moves to block kb.
+__device__ __forceinline__ uint32_t i8_pixel_yoff(const I8Params &p, int m, int half) {
+  if (m >= p.M) return OOB_OFFSET;
+  const int n = m / p.PQ;
+  const int pq = m - n * p.PQ;
+  return (uint32_t)((n * p.KBLK * p.PQ + pq) * 32 + 16 * half);
+}
+
+// One 32x32 accumulator tile (rows = output channels of 32-channel block
+// kb, columns = 32 output pixels) into y in NCxHWx<32> over K.
 // Accumulator layout of v_mfma_i32_32x32x32_i8: lane l, register i holds
 // D[row = 8*(i/4) + 4*(l/32) + i%4][col = l%32], so the quad i = 4g..4g+3
 // packs into the dword at byte 8g + 4*(l/32) of pixel l%32's 32 channels.
 // Lanes l and l+32 together hold a pixel's 32 bytes; two lane-half swaps
 // (v_permlane32_swap) give lane l bytes 0..15 and lane l+32 bytes 16..31,
-// so each tile leaves in one 16-byte store per lane: 32 consecutive pixels,
-// 1 KiB contiguous when they share an image.
-//   m_base: first pixel of fragment column 0; kb_base: first 32-channel
-//   block of fragment row 0.  Pixels past M and blocks past K/32 are skipped.
-// One 32x32 accumulator tile (rows = output channels of 32-channel block
-// kb, columns = output pixels m_col .. m_col+31) into y in NCxHWx<32> over K.
-__device__ __forceinline__ void store_i8_frag(const v16i &v, int8_t *__restrict__ y,
-                                              const I8Params &p, int m_col, int kb, int lane) {
-  const int half = lane >> 5;
-  const int l32 = lane & 31;
+// so the tile leaves in one 16-byte store per lane: 32 consecutive pixels,
+// 1 KiB contiguous when they share an image.  yoff is i8_pixel_yoff() of
+// the lane's pixel; the store goes through a buffer descriptor over y, so
+// pixels past M and blocks past K/32 (offset OOB_OFFSET) are dropped
+// without a branch.
+__device__ __forceinline__ void store_i8_frag(const v16i &v, __amdgpu_buffer_rsrc_t yr,
+                                              uint32_t yoff, int kb, const I8Params &p) {
   const float alpha = p.alpha;
-  const int m = m_col + l32;
   uint32_t d[4];
 #pragma unroll
   for (int g = 0; g < 4; ++g)
     d[g] = pack_low_bytes(i8_epilogue_bits(v[4 * g + 0], alpha), i8_epilogue_bits(v[4 * g + 1], alpha),
                           i8_epilogue_bits(v[4 * g + 2], alpha), i8_epilogue_bits(v[4 * g + 3], alpha));
-  // (upper half of d0) <-> (lower half of d2), likewise d1 / d3; every lane
-  // takes part, before any per-lane predicate
+  // (upper half of d0) <-> (lower half of d2), likewise d1 / d3
   const auto s02 = __builtin_amdgcn_permlane32_swap(d[0], d[2], false, false);
   const auto s13 = __builtin_amdgcn_permlane32_swap(d[1], d[3], false, false);
-  if (kb < p.KBLK && m < p.M) {
-    const int n = m / p.PQ;
-    const int pq = m - n * p.PQ;
-    int8_t *dst = y + ((size_t)(n * p.KBLK + kb) * p.PQ + pq) * 32 + 16 * half;
-    *reinterpret_cast<v4i *>(dst) = v4i{(int)s02[0], (int)s02[1], (int)s13[0], (int)s13[1]};
-  }
+  const uint32_t off = kb < p.KBLK && yoff != OOB_OFFSET ? yoff + (uint32_t)(kb * p.PQ * 32) : OOB_OFFSET;
+  __builtin_amdgcn_raw_buffer_store_b128(v4i{(int)s02[0], (int)s02[1], (int)s13[0], (int)s13[1]},
+                                         yr, off, 0, 0);
 }
 
 // An FK x FP grid of tiles: fragment (a, b) covers channel block kb_base + a
@@ -80,10 +82,13 @@ template <int FK, int FP>
 __device__ __forceinline__ void store_i8_tile(const v16i (&acc)[FK][FP], int8_t *__restrict__ y,
                                               const I8Params &p, int m_base, int kb_base,
                                               int lane) {
+  const __amdgpu_buffer_rsrc_t yr = make_rsrc(y, p.y_bytes);
 #pragma unroll
-  for (int b = 0; b < FP; ++b)
+  for (int b = 0; b < FP; ++b) {
+    const uint32_t yoff = i8_pixel_yoff(p, m_base + 32 * b + (lane & 31), lane >> 5);
 #pragma unroll
-    for (int a = 0; a < FK; ++a) store_i8_frag(acc[a][b], y, p, m_base + 32 * b, kb_base + a, lane);
+    for (int a = 0; a < FK; ++a) store_i8_frag(acc[a][b], yr, yoff, kb_base + a, p);
+  }
 }
 
 }  // namespace convfprop

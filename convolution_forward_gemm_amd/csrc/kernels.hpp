@@ -19,7 +19,7 @@ struct I8Params {
   int ntaps;    // CB*R*S reduction steps of 32 channels
   int ph, pw, sh, sw, dh, dw;
   int k_tiles;  // workgroup tiles along K
-  uint32_t x_bytes, w_bytes;
+  uint32_t x_bytes, w_bytes, y_bytes;
   float alpha;
   // Halo kernel only (see conv_i8_halo.hip): virtual rows per image, halo
   // columns, halo DMA blocks per half-plane, LDS bytes per stage and total.

@@ -191,11 +191,23 @@ def cpu_baseline(wk, x, w):
         passes += 1
     P, Q = acc.shape[2:]
     ops = passes * 2 * n * wk.K * P * Q * wk.C * wk.R * wk.S
+    # the same oracle on one thread, over one image
+    t0 = time.perf_counter()
+    oracle.conv2d_i8(x[:1], w, wk.alpha, **wk.conv_kwargs, nthreads=1)
+    dt1 = time.perf_counter() - t0
+    ops1 = 2 * wk.K * P * Q * wk.C * wk.R * wk.S
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = None
     return {"value": round(ops / dt / 1e12, 6), "unit": "TOPS", "cores": threads,
             "kind": "oracle",
             "sample": "%d pass(es) over %d of %d images of the headline workload (all %d output "
                       "channels, %dx%d outputs), int64 accumulation + epilogue; %.1f s"
-                      % (passes, n, wk.N, wk.K, P, Q, dt)}
+                      % (passes, n, wk.N, wk.K, P, Q, dt),
+            "single_thread_value": round(ops1 / dt1 / 1e12, 6),
+            "single_thread_sample": "1 image, %.2f s" % dt1,
+            "nproc": os.cpu_count(), "affinity_cpus": affinity}
 
 
 # ---------------------------------------------------------------------------

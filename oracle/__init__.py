@@ -65,6 +65,10 @@ def _load(path=None):
         lib.oracle_conv2d_i8_points.restype = i32
         lib.oracle_epilogue_i8.argtypes = [p, p, i64, ctypes.c_float]
         lib.oracle_epilogue_i8.restype = i32
+        lib.oracle_epilogue_i8_per_channel.argtypes = [p, p, i32, i32, i64, p, p]
+        lib.oracle_epilogue_i8_per_channel.restype = i32
+        lib.oracle_epilogue_f32_per_channel.argtypes = [p, p, i32, i32, i64, p, p]
+        lib.oracle_epilogue_f32_per_channel.restype = None
         lib.oracle_conv2d_f32_acc.argtypes = [p, p, p] + conv_args
         lib.oracle_conv2d_f32_acc.restype = i32
         lib.oracle_conv2d_f32_points.argtypes = [p, p, p, i64, p] + conv_args
@@ -175,6 +179,49 @@ def conv2d_i8(x, w, alpha, pad=0, stride=1, dil=1, nthreads=1):
     """(acc int64, y int8) of the int8 conv fprop, all in logical NCHW/KCRS/NKPQ."""
     acc = conv2d_i8_acc(x, w, pad, stride, dil, nthreads)
     return acc, epilogue_i8(acc, alpha)
+
+
+def _per_channel(alpha_k, bias_k, K):
+    a = np.ascontiguousarray(alpha_k, dtype=np.float32).reshape(-1)
+    if a.size != K:
+        raise ValueError("alpha_k needs %d values" % K)
+    b = None
+    if bias_k is not None:
+        b = np.ascontiguousarray(bias_k, dtype=np.float32).reshape(-1)
+        if b.size != K:
+            raise ValueError("bias_k needs %d values" % K)
+    return a, b
+
+
+def epilogue_i8_per_channel(acc, alpha_k, bias_k=None) -> np.ndarray:
+    """clamp(rint(fl32(fl32(fl32(acc) * alpha[k]) + bias[k])), -128, 127) as
+    int8 over acc in logical NKPQ (the per-output-channel variant)."""
+    acc = np.ascontiguousarray(acc, dtype=np.int64)
+    N, K = acc.shape[:2]
+    a, b = _per_channel(alpha_k, bias_k, K)
+    y = np.empty(acc.shape, dtype=np.int8)
+    plane = int(np.prod(acc.shape[2:]))
+    rc = _load().oracle_epilogue_i8_per_channel(_ptr(acc), _ptr(y), N, K, plane, _ptr(a),
+                                                _ptr(b) if b is not None else None)
+    if rc:
+        raise OracleError("oracle_epilogue_i8_per_channel failed: %d" % rc)
+    return y
+
+
+def conv2d_i8_scaled(x, w, alpha_k, bias_k=None, pad=0, stride=1, dil=1, nthreads=1):
+    """(acc int64, y int8) with the per-output-channel scale and bias."""
+    acc = conv2d_i8_acc(x, w, pad, stride, dil, nthreads)
+    return acc, epilogue_i8_per_channel(acc, alpha_k, bias_k)
+
+
+def epilogue_f32_per_channel(acc, alpha_k, bias_k=None) -> np.ndarray:
+    acc = np.ascontiguousarray(acc, dtype=np.float64)
+    N, K = acc.shape[:2]
+    a, b = _per_channel(alpha_k, bias_k, K)
+    y = np.empty(acc.shape, dtype=np.float32)
+    _load().oracle_epilogue_f32_per_channel(_ptr(acc), _ptr(y), N, K, int(np.prod(acc.shape[2:])),
+                                            _ptr(a), _ptr(b) if b is not None else None)
+    return y
 
 
 def conv2d_f32_acc(x, w, pad=0, stride=1, dil=1, nthreads=1) -> np.ndarray:

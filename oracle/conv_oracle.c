@@ -162,6 +162,49 @@ int oracle_epilogue_i8(const int64_t *acc, int8_t *y, int64_t count, float alpha
     return ORACLE_OK;
 }
 
+/* Per-output-channel epilogue variant: a scale alpha[k] and a bias bias[k]
+ * for each output channel k (bias may be NULL for none).  Source: the
+ * "rowwise scaled" operators named in the review thread of torchao issue
+ * 1406 (PR 1515, CUTLASS-based W4A8/W4A4 GEMM), read as a scale per GEMM
+ * column, which is an output channel here, plus a bias per column:
+ *   y[n][k][p][q] = clamp(rint(fl32(fl32(fl32(acc) * alpha[k]) + bias[k])), -128, 127)
+ * (one fp32 multiply, then one fp32 add; no fused multiply-add).  acc is
+ * logical NKPQ int64 with plane = P*Q. */
+int oracle_epilogue_i8_per_channel(const int64_t *acc, int8_t *y, int N, int K, int64_t plane,
+                                   const float *alpha, const float *bias)
+{
+    if (fegetround() != FE_TONEAREST) return ORACLE_ERR_ROUNDING;
+    if (N <= 0 || K <= 0 || plane <= 0) return ORACLE_ERR_SHAPE;
+    for (int64_t i = 0; i < (int64_t)N * K * plane; ++i)
+        if (acc[i] > INT32_MAX || acc[i] < INT32_MIN) return ORACLE_ERR_RANGE;
+    for (int n = 0; n < N; ++n)
+        for (int k = 0; k < K; ++k)
+            for (int64_t j = 0; j < plane; ++j) {
+                const int64_t i = ((int64_t)n * K + k) * plane + j;
+                volatile float f = (float)(int32_t)acc[i];
+                volatile float g = f * alpha[k];
+                volatile float h = g + (bias ? bias[k] : 0.0f);
+                float r = rintf(h);
+                if (r > 127.0f) r = 127.0f;
+                if (r < -128.0f) r = -128.0f;
+                y[i] = (int8_t)r;
+            }
+    return ORACLE_OK;
+}
+
+/* fp32 per-output-channel variant: y = alpha[k] * acc + bias[k] (bias may be
+ * NULL), computed in double from the double accumulator, rounded once. */
+void oracle_epilogue_f32_per_channel(const double *acc, float *y, int N, int K, int64_t plane,
+                                     const float *alpha, const float *bias)
+{
+    for (int n = 0; n < N; ++n)
+        for (int k = 0; k < K; ++k)
+            for (int64_t j = 0; j < plane; ++j) {
+                const int64_t i = ((int64_t)n * K + k) * plane + j;
+                y[i] = (float)((double)alpha[k] * acc[i] + (bias ? (double)bias[k] : 0.0));
+            }
+}
+
 /* One fp32 output, each product exact in double, summed in double. */
 static double acc_f32_point(const float *x, const float *w, int n, int k, int p,
                             int q, int C, int H, int W, int R, int S, int ph,

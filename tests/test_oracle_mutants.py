@@ -36,6 +36,11 @@ MUTANTS = {
     "output_dim_off_by_one": ("return (int)(num / stride + 1);", "return (int)(num / stride);"),
     "f32_float_accumulator": ("double acc = 0.0;\n    for (int c = 0; c < C; ++c)",
                               "float acc = 0.0f;\n    for (int c = 0; c < C; ++c)"),
+    "per_channel_bias_after_rounding": ("volatile float h = g + (bias ? bias[k] : 0.0f);\n                float r = rintf(h);",
+                                        "volatile float h = g;\n                float r = rintf(h) + (bias ? bias[k] : 0.0f);"),
+    "per_channel_wrong_channel": ("volatile float g = f * alpha[k];", "volatile float g = f * alpha[(k + 1) % K];"),
+    "per_channel_fused": ("volatile float g = f * alpha[k];\n                volatile float h = g + (bias ? bias[k] : 0.0f);",
+                          "volatile float g = 0.0f;\n                volatile float h = fmaf(f, alpha[k], bias ? bias[k] : 0.0f) + g;"),
     "layout_hw_swapped": ("dst[((((size_t)n * (C / 32) + c / 32) * H + h) * W + w) * 32 + c % 32] =",
                           "dst[((((size_t)n * (C / 32) + c / 32) * W + w) * H + h) * 32 + c % 32] ="),
     "filter_layout_rs_swapped": ("dst[((((size_t)(c / 32) * R + r) * S + s) * K + k) * 32 + c % 32] =",
@@ -61,6 +66,11 @@ def _battery():
         ("layout_hand", pins.test_nc32hw32_hand_listed, ()),
         ("filter_layout_hand", pins.test_c32rsk32_hand_listed, ()),
         ("layout_numpy", pins.test_layout_maps_match_numpy_reshape, ()),
+        ("per_channel_hand", pins.test_per_channel_hand_values, ()),
+        ("per_channel_two_roundings", pins.test_per_channel_multiply_then_add_rounds_twice, ()),
+        ("per_channel_c1", pins.test_per_channel_c1_all_ones_with_bias, ()),
+        ("per_channel_scalar", pins.test_per_channel_with_one_scale_is_the_scalar_epilogue, ()),
+        ("f32_per_channel_hand", pins.test_f32_per_channel_hand_values, ()),
     ]
     for acc, alpha, expect in [(2088960, 2.0 ** -14, 127), (-2105344, 2.0 ** -14, -128),
                                (40960, 2.0 ** -14, 2), (25, 0.1, 2)]:

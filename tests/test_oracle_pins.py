@@ -455,3 +455,74 @@ def test_layout_maps_match_numpy_reshape():
 def test_layout_rejects_non_multiple_of_32():
     with pytest.raises(oracle.OracleError):
         oracle.nchw_to_nc32hw32(np.zeros((1, 48, 2, 2), np.int8))
+
+
+# --------------------------------------------------------------------------
+# Per-output-channel scale and bias (the "rowwise scaled" epilogue variant):
+# y = clamp(rint(fl32(fl32(fl32(acc) * alpha[k]) + bias[k])), -128, 127).
+# Expected values are worked by hand below.
+# --------------------------------------------------------------------------
+def test_per_channel_hand_values():
+    acc = np.array([64, 96], np.int64).reshape(1, 2, 1, 1)
+    # channel 0: 64 * 0.5 = 32, + 0.25 = 32.25 -> 32
+    # channel 1: 96 * 0.25 = 24, - 0.5 = 23.5 -> 24 (tie to even)
+    assert oracle.epilogue_i8_per_channel(acc, [0.5, 0.25], [0.25, -0.5]).ravel().tolist() == [32, 24]
+    # swapped per-channel values must move with their channel:
+    # channel 0: 64 * 0.25 = 16, - 0.5 = 15.5 -> 16; channel 1: 96 * 0.5 + 0.25 = 48.25 -> 48
+    assert oracle.epilogue_i8_per_channel(acc, [0.25, 0.5], [-0.5, 0.25]).ravel().tolist() == [16, 48]
+    # no bias: the scale alone
+    assert oracle.epilogue_i8_per_channel(acc, [0.5, 0.25]).ravel().tolist() == [32, 24]
+    # saturation through the bias
+    one = np.ones((1, 2, 1, 1), np.int64)
+    assert oracle.epilogue_i8_per_channel(one, [1.0, 1.0], [200.0, -300.0]).ravel().tolist() == [127, -128]
+
+
+def test_per_channel_multiply_then_add_rounds_twice():
+    # fl32(1/7) = 0.14285714924335479736328125; 7 * that = 1 + 0.75 * 2**-24,
+    # which rounds to 1.0 in fp32 (a quarter ulp below the midpoint); 1.0 - 0.5
+    # = 0.5 -> rint 0.  A fused multiply-add would round 0.5 + 0.75 * 2**-24
+    # once, to 0.5 + 2**-24, and give 1.
+    acc = np.array([7], np.int64).reshape(1, 1, 1, 1)
+    a = float(np.float32(1.0 / 7.0))
+    assert a == 0.14285714924335479736328125
+    assert oracle.epilogue_i8_per_channel(acc, [a], [-0.5]).ravel().tolist() == [0]
+
+
+def test_per_channel_c1_all_ones_with_bias():
+    # c1 with x = w = 1: acc 288 (interior, 36 per plane), 192 (edge, 24),
+    # 128 (corner, 4); alpha = 1/64 gives 4.5, 3, 2.  Bias by channel k % 3:
+    #   +0.25: 4.75 -> 5, 3.25 -> 3, 2.25 -> 2
+    #   -0.5 : 4.0  -> 4, 2.5  -> 2, 1.5  -> 2
+    #   +0.5 : 5.0  -> 5, 3.5  -> 4, 2.5  -> 2
+    x = np.ones((1, 32, 8, 8), np.int8)
+    w = np.ones((32, 32, 3, 3), np.int8)
+    bias = np.array([(0.25, -0.5, 0.5)[k % 3] for k in range(32)], np.float32)
+    acc, y = oracle.conv2d_i8_scaled(x, w, np.full(32, 2.0 ** -6, np.float32), bias, pad=1)
+    expect = {0: (5, 3, 2), 1: (4, 2, 2), 2: (5, 4, 2)}
+    for k in range(32):
+        yi, ye, yc = expect[k % 3]
+        yk = y[0, k]
+        assert yk[3, 3] == yi and yk[0, 3] == ye and yk[0, 0] == yc
+        vals, counts = np.unique(yk, return_counts=True)
+        want = {}
+        for v, c in ((yi, 36), (ye, 24), (yc, 4)):
+            want[v] = want.get(v, 0) + c
+        assert dict(zip(vals.tolist(), counts.tolist())) == want
+
+
+def test_per_channel_with_one_scale_is_the_scalar_epilogue():
+    # every channel with the same alpha and no bias reduces to the pinned
+    # scalar epilogue
+    r = np.random.default_rng(11)
+    acc = r.integers(-2 ** 26, 2 ** 26, size=(2, 5, 3, 4), dtype=np.int64)
+    for alpha in (2.0 ** -14, 0.1, 1.0 / 3.0):
+        a = np.full(5, alpha, np.float32)
+        assert np.array_equal(oracle.epilogue_i8_per_channel(acc, a), oracle.epilogue_i8(acc, alpha))
+
+
+def test_f32_per_channel_hand_values():
+    acc = np.array([3.0, -5.0, 7.0, 11.0], np.float64).reshape(1, 2, 1, 2)
+    # channel 0: 0.5 * 3 + 0.25 = 1.75, 0.5 * -5 + 0.25 = -2.25
+    # channel 1: -2 * 7 + 1 = -13, -2 * 11 + 1 = -21
+    y = oracle.epilogue_f32_per_channel(acc, [0.5, -2.0], [0.25, 1.0])
+    assert y.ravel().tolist() == [1.75, -2.25, -13.0, -21.0]

@@ -18,6 +18,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -464,6 +466,15 @@ def main():
         t4 = conv_ops(w4, c4.P, c4.Q) / (ms4 * 1e-3) / 1e12
         extra["c4_strided"] = {"ms": round(ms4, 6), "TOPS": round(t4, 3),
                                "pct_of_int8_peak": round(100 * t4 / PEAK_INT8_TOPS, 2), "config": c4.config}
+        # per-output-channel scale and bias (conv2d_fprop_run_scaled) on the
+        # headline workload
+        gen = np.random.default_rng((2026, 31, 3))
+        al = torch.from_numpy((wk.alpha * gen.uniform(0.5, 2.0, wk.K)).astype(np.float32)).cuda()
+        bi = torch.from_numpy(gen.uniform(-3.0, 3.0, wk.K).astype(np.float32)).cuda()
+        mss = time_device(torch, lambda: conv.run_scaled_ptr(xp, wp, yp, al.data_ptr(), bi.data_ptr(),
+                                                             stream), 2000, 500)
+        extra["c3_per_channel_scale_bias"] = {"ms": round(mss, 6),
+                                              "TOPS": round(ops / (mss * 1e-3) / 1e12, 3)}
         # cold operands: rotate through enough copies of x, w, y that the
         # 256 MB Infinity Cache (and every L2) holds none of a call's operands
         # when it starts (more than twice the cache in total)

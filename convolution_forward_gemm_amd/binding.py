@@ -49,6 +49,7 @@ SIGNATURES = {
     "conv2d_fprop_num_configs": (_i, [_i]),
     "conv2d_fprop_desc_set_config": (_i, [_p, _i]),
     "conv2d_fprop_run": (_i, [_p, _p, _p, _p, _f, _p]),
+    "conv2d_fprop_run_scaled": (_i, [_p, _p, _p, _p, _p, _p, _p]),
     "conv_nchw_to_nc32hw32_i8": (_i, [_p, _p, _i, _i, _i, _i, _p]),
     "conv_nc32hw32_to_nchw_i8": (_i, [_p, _p, _i, _i, _i, _i, _p]),
     "conv_kcrs_to_c32rsk32_i8": (_i, [_p, _p, _i, _i, _i, _i, _p]),
@@ -158,6 +159,34 @@ class Conv2dFprop:
         """Launch on raw device pointers (no Python-side checks)."""
         _check(lib.conv2d_fprop_run(self._h, x_ptr, w_ptr, y_ptr, alpha, stream_handle),
                "conv2d_fprop_run")
+
+    def run_scaled_ptr(self, x_ptr: int, w_ptr: int, y_ptr: int, alpha_ptr: int, bias_ptr,
+                       stream_handle: int = 0):
+        """Per-output-channel scale (and bias, or None) on raw device pointers."""
+        _check(lib.conv2d_fprop_run_scaled(self._h, x_ptr, w_ptr, y_ptr, alpha_ptr, bias_ptr,
+                                           stream_handle), "conv2d_fprop_run_scaled")
+
+    def run_scaled(self, x, w, alpha, bias=None, y=None, stream=None):
+        """y <- conv(x, w) with alpha[k] and bias[k] per output channel:
+        contiguous float32 CUDA tensors of K values (bias may be None)."""
+        import torch
+        for name, t in (("alpha", alpha), ("bias", bias)):
+            if t is None and name == "bias":
+                continue
+            if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous() or t.numel() != self.K:
+                raise ValueError("%s must be a contiguous float32 CUDA tensor of %d values" % (name, self.K))
+        tdt = torch.int8 if self.dtype == "int8" else torch.float32
+        for name, t, shape in (("x", x, self.x_shape), ("w", w, self.w_shape)):
+            if t.dtype != tdt or not t.is_cuda or not t.is_contiguous() or t.numel() != _prod(shape):
+                raise ValueError("%s must be a contiguous %s CUDA tensor with %d elements"
+                                 % (name, tdt, _prod(shape)))
+        if y is None:
+            y = torch.empty(self.y_shape, dtype=tdt, device=x.device)
+        elif y.dtype != tdt or not y.is_cuda or not y.is_contiguous() or y.numel() != _prod(self.y_shape):
+            raise ValueError("y must be a contiguous %s CUDA tensor of shape %s" % (tdt, self.y_shape))
+        self.run_scaled_ptr(x.data_ptr(), w.data_ptr(), y.data_ptr(), alpha.data_ptr(),
+                            bias.data_ptr() if bias is not None else None, _stream_handle(stream))
+        return y
 
     def run(self, x, w, y=None, alpha: float = 1.0, stream=None):
         """y <- conv(x, w) on the GPU.  Tensors are torch CUDA tensors in the

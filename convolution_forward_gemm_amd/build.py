@@ -63,9 +63,20 @@ def device_asm(source: str, verbose: bool = False) -> str:
 
 
 def build(verbose: bool = False) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    """Compile every source to an object in parallel, then link the library."""
+    import concurrent.futures
+    import tempfile
+    cflags = [f for f in FLAGS if f != "-shared"]
     tmp = LIB + ".tmp%d" % os.getpid()
-    _run([HIPCC, *FLAGS, *srcs, "-o", tmp], verbose)
+    with tempfile.TemporaryDirectory() as d:
+        def compile_one(src):
+            obj = os.path.join(d, src + ".o")
+            _run([HIPCC, *cflags, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+            return obj
+        workers = max(1, min(len(SOURCES), os.cpu_count() or 1))
+        with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
+            objs = list(ex.map(compile_one, SOURCES))
+        _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 

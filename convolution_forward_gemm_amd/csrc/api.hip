@@ -395,28 +395,58 @@ conv_status_t conv2d_fprop_desc_set_config(conv2d_fprop_desc_t d, int config) {
   return CONV_OK;
 }
 
-conv_status_t conv2d_fprop_run(conv2d_fprop_desc_t d, const void *x, const void *w,
-                               void *y, float alpha, hipStream_t stream) {
+static conv_status_t run_impl(conv2d_fprop_desc_t d, const void *x, const void *w, void *y,
+                              float alpha, const float *alpha_k, const float *bias_k,
+                              hipStream_t stream) {
+  hipError_t e;
+  if (d->dtype == CONV_DTYPE_INT8) {
+    I8Params p = d->i8;
+    p.alpha = alpha;
+    p.alpha_k = alpha_k;
+    p.bias_k = bias_k;
+    e = i8_config(d->config)->launch((const int8_t *)x, (const int8_t *)w, (int8_t *)y, p,
+                                     d->grid, stream);
+  } else {
+    F32Params p = d->f32;
+    p.alpha = alpha;
+    p.alpha_k = alpha_k;
+    p.bias_k = bias_k;
+    e = kF32Configs[d->config].launch((const float *)x, (const float *)w, (float *)y, p,
+                                      d->grid, stream);
+  }
+  return e == hipSuccess ? CONV_OK : CONV_ERR_HIP;
+}
+
+static conv_status_t check_run(conv2d_fprop_desc_t d, const void *x, const void *w,
+                               const void *y) {
   if (!d || !x || !w || !y) return CONV_ERR_NULL;
   const uintptr_t align = d->dtype == CONV_DTYPE_INT8 ? 16 : 4;
   if (((uintptr_t)x | (uintptr_t)w | (uintptr_t)y) & (align - 1)) return CONV_ERR_MISALIGNED;
   if (ranges_overlap(x, d->x_bytes, y, d->y_bytes) ||
       ranges_overlap(w, d->w_bytes, y, d->y_bytes))
     return CONV_ERR_UNSUPPORTED;
+  return CONV_OK;
+}
+
+conv_status_t conv2d_fprop_run(conv2d_fprop_desc_t d, const void *x, const void *w,
+                               void *y, float alpha, hipStream_t stream) {
+  const conv_status_t st = check_run(d, x, w, y);
+  if (st != CONV_OK) return st;
   if (d->dtype == CONV_DTYPE_INT8 && !isfinite(alpha)) return CONV_ERR_INVALID_ALPHA;
-  hipError_t e;
-  if (d->dtype == CONV_DTYPE_INT8) {
-    I8Params p = d->i8;
-    p.alpha = alpha;
-    e = i8_config(d->config)->launch((const int8_t *)x, (const int8_t *)w, (int8_t *)y, p,
-                                     d->grid, stream);
-  } else {
-    F32Params p = d->f32;
-    p.alpha = alpha;
-    e = kF32Configs[d->config].launch((const float *)x, (const float *)w, (float *)y, p,
-                                      d->grid, stream);
-  }
-  return e == hipSuccess ? CONV_OK : CONV_ERR_HIP;
+  return run_impl(d, x, w, y, alpha, nullptr, nullptr, stream);
+}
+
+conv_status_t conv2d_fprop_run_scaled(conv2d_fprop_desc_t d, const void *x, const void *w,
+                                      void *y, const float *alpha, const float *bias,
+                                      hipStream_t stream) {
+  const conv_status_t st = check_run(d, x, w, y);
+  if (st != CONV_OK) return st;
+  if (!alpha) return CONV_ERR_NULL;
+  if (((uintptr_t)alpha | (uintptr_t)bias) & 15) return CONV_ERR_MISALIGNED;
+  const int64_t kb = (int64_t)d->K * 4;
+  if (ranges_overlap(alpha, kb, y, d->y_bytes) || (bias && ranges_overlap(bias, kb, y, d->y_bytes)))
+    return CONV_ERR_UNSUPPORTED;
+  return run_impl(d, x, w, y, 1.0f, alpha, bias, stream);
 }
 
 // ---- layout transforms ----------------------------------------------------

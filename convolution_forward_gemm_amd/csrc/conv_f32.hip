@@ -238,9 +238,11 @@ conv_f32_kernel(const float *__restrict__ x, const float *__restrict__ w,
     }
   }
 
-  // ---- epilogue: y[n][k][p][q] = alpha * acc ------------------------------
+  // ---- epilogue: y[n][k][p][q] = alpha * acc (+ per channel: alpha[k] * acc
+  // + bias[k], one multiply then one add) --------------------------------------
   // Accumulator layout of v_mfma_f32_32x32x2_f32: lane l, register i holds
   // D[row = 8*(i/4) + 4*(l/32) + i%4][col = l%32]; rows are channels.
+  const float *alpha_k = p.alpha_k, *bias_k = p.bias_k;
 #pragma unroll
   for (int b = 0; b < FP; ++b) {
     const int m = m0 + 32 * (wave * FP + b) + l32;
@@ -252,7 +254,11 @@ conv_f32_kernel(const float *__restrict__ x, const float *__restrict__ w,
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int k = k0 + 32 * a + 8 * (i / 4) + 4 * half + (i % 4);
-        if (k < p.K) y[((size_t)n * p.K + k) * p.PQ + pq] = alpha * acc[a][b][i];
+        if (k < p.K) {
+          float v = (alpha_k ? alpha_k[k] : alpha) * acc[a][b][i];
+          if (bias_k) v = v + bias_k[k];
+          y[((size_t)n * p.K + k) * p.PQ + pq] = v;
+        }
       }
   }
 }

@@ -162,7 +162,7 @@ __device__ __forceinline__ TapDesc pick_tap(const TapDesc (&td)[KT], int t) {
 // the channel block inner, which needs C/32 % KT == 0: every stage then has a
 // single filter position, so the padding mask is evaluated once per stage and
 // the KT loads of a lane differ only in a wave-uniform offset.
-template <int WK, int WP, int FK, int FP, int KT, int NS, bool RSO>
+template <int WK, int WP, int FK, int FP, int KT, int NS, bool RSO, bool PC>
 __global__ void __launch_bounds__(64 * WK * WP)
 conv_i8_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ w,
                int8_t *__restrict__ y, I8Params p) {
@@ -392,23 +392,31 @@ conv_i8_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ w,
   }
   wait_vm_lgkm0<0>();  // no LDS-DMA may outlive the workgroup
 
-  store_i8_tile<FK, FP>(acc, y, p, m0 + 32 * wp * FP, k0 / 32 + wk * FK, lane);
+  store_i8_tile<PC, FK, FP>(acc, y, p, m0 + 32 * wp * FP, k0 / 32 + wk * FK, lane);
 }
 
 // ---------------------------------------------------------------------------
 // Configuration table.  Each entry is one compiled tile shape.
 // ---------------------------------------------------------------------------
+template <int WK, int WP, int FK, int FP, int KT, int NS, bool RSO, bool PC>
+static hipError_t launch_i8_pc(const int8_t *x, const int8_t *w, int8_t *y,
+                               const I8Params &p, int grid, hipStream_t s) {
+  using T = I8Tile<WK, WP, FK, FP, KT, NS>;
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void *>(&conv_i8_kernel<WK, WP, FK, FP, KT, NS, RSO, PC>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS_BYTES);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL((conv_i8_kernel<WK, WP, FK, FP, KT, NS, RSO, PC>), dim3(grid),
+                     dim3(T::THREADS), T::LDS_BYTES, s, x, w, y, p);
+  return hipGetLastError();
+}
+
+// Launch with the per-output-channel epilogue when the call carries one.
 template <int WK, int WP, int FK, int FP, int KT, int NS, bool RSO>
 static hipError_t launch_i8(const int8_t *x, const int8_t *w, int8_t *y,
                             const I8Params &p, int grid, hipStream_t s) {
-  using T = I8Tile<WK, WP, FK, FP, KT, NS>;
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void *>(&conv_i8_kernel<WK, WP, FK, FP, KT, NS, RSO>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS_BYTES);
-  if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((conv_i8_kernel<WK, WP, FK, FP, KT, NS, RSO>), dim3(grid),
-                     dim3(T::THREADS), T::LDS_BYTES, s, x, w, y, p);
-  return hipGetLastError();
+  return p.alpha_k ? launch_i8_pc<WK, WP, FK, FP, KT, NS, RSO, true>(x, w, y, p, grid, s)
+                   : launch_i8_pc<WK, WP, FK, FP, KT, NS, RSO, false>(x, w, y, p, grid, s);
 }
 
 #define I8_CFG(WK, WP, FK, FP, KT, NS, RSO)                                     \

@@ -66,7 +66,7 @@ __device__ __forceinline__ void halo_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int WK, int WP, int FK, int FP, int R, int S, int NS, int HJ>
+template <int WK, int WP, int FK, int FP, int R, int S, int NS, int HJ, bool PC>
 __global__ void __launch_bounds__(64 * WK * WP)
 conv_i8_halo_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ w,
                     int8_t *__restrict__ y, I8Params p) {
@@ -246,7 +246,7 @@ conv_i8_halo_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ w,
   }
   halo_wait<0>();  // no LDS-DMA may outlive the workgroup
 
-  store_i8_tile<FK, FP>(acc, y, p, m0 + 32 * wp * FP, k0 / 32 + wk * FK, lane);
+  store_i8_tile<PC, FK, FP>(acc, y, p, m0 + 32 * wp * FP, k0 / 32 + wk * FK, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -321,7 +321,8 @@ struct HaloAdTile {
   static_assert(WAIT0 < 64 && WAITL < 64, "vmcnt counts at most 63 outstanding loads");
 };
 
-template <int WK, int WP, int FK, int FP, int R, int S, int NS, int HJ, int PW, int CPS, int AL>
+template <int WK, int WP, int FK, int FP, int R, int S, int NS, int HJ, int PW, int CPS, int AL,
+          bool PC>
 __global__ void __launch_bounds__(64 * WK * WP)
 conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ w,
                        int8_t *__restrict__ y, I8Params p) {
@@ -636,24 +637,46 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
                                                             acc[a][b], 0, 0, 0);
       }
 #pragma unroll
-      for (int a = 0; a < FK; ++a) store_i8_frag(acc[a][b], yr, y_off[b], kb_wave + a, p);
+      for (int a = 0; a < FK; ++a) store_i8_frag<PC>(acc[a][b], yr, y_off[b], kb_wave + a, p);
     }
     halo_wait<0>();  // no LDS-DMA (of the ring's idle stages) may outlive the workgroup
   } else {
     halo_wait<0>();
-    store_i8_tile<FK, FP>(acc, y, p, m_wave, kb_wave, lane);
+    store_i8_tile<PC, FK, FP>(acc, y, p, m_wave, kb_wave, lane);
   }
+}
+
+template <int WK, int WP, int FK, int FP, int R, int S, int NS, int HJ, int PW, int CPS, int AL,
+          bool PC>
+static hipError_t launch_i8_halo_ad_pc(const int8_t *x, const int8_t *w, int8_t *y,
+                                       const I8Params &p, int grid, hipStream_t s) {
+  using T = HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL>;
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void *>(&conv_i8_halo_ad_kernel<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, PC>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL((conv_i8_halo_ad_kernel<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, PC>), dim3(grid),
+                     dim3(T::THREADS), p.lds_bytes, s, x, w, y, p);
+  return hipGetLastError();
 }
 
 template <int WK, int WP, int FK, int FP, int R, int S, int NS, int HJ, int PW, int CPS, int AL>
 static hipError_t launch_i8_halo_ad(const int8_t *x, const int8_t *w, int8_t *y,
                                     const I8Params &p, int grid, hipStream_t s) {
-  using T = HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL>;
+  return p.alpha_k
+             ? launch_i8_halo_ad_pc<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, true>(x, w, y, p, grid, s)
+             : launch_i8_halo_ad_pc<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, false>(x, w, y, p, grid, s);
+}
+
+template <int WK, int WP, int FK, int FP, int R, int S, int NS, int HJ, bool PC>
+static hipError_t launch_i8_halo_pc(const int8_t *x, const int8_t *w, int8_t *y,
+                                    const I8Params &p, int grid, hipStream_t s) {
+  using T = HaloTile<WK, WP, FK, FP, R, S, NS, HJ>;
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void *>(&conv_i8_halo_ad_kernel<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL>),
+      reinterpret_cast<const void *>(&conv_i8_halo_kernel<WK, WP, FK, FP, R, S, NS, HJ, PC>),
       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((conv_i8_halo_ad_kernel<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL>), dim3(grid),
+  hipLaunchKernelGGL((conv_i8_halo_kernel<WK, WP, FK, FP, R, S, NS, HJ, PC>), dim3(grid),
                      dim3(T::THREADS), p.lds_bytes, s, x, w, y, p);
   return hipGetLastError();
 }
@@ -661,14 +684,8 @@ static hipError_t launch_i8_halo_ad(const int8_t *x, const int8_t *w, int8_t *y,
 template <int WK, int WP, int FK, int FP, int R, int S, int NS, int HJ>
 static hipError_t launch_i8_halo(const int8_t *x, const int8_t *w, int8_t *y,
                                  const I8Params &p, int grid, hipStream_t s) {
-  using T = HaloTile<WK, WP, FK, FP, R, S, NS, HJ>;
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void *>(&conv_i8_halo_kernel<WK, WP, FK, FP, R, S, NS, HJ>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-  if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((conv_i8_halo_kernel<WK, WP, FK, FP, R, S, NS, HJ>), dim3(grid),
-                     dim3(T::THREADS), p.lds_bytes, s, x, w, y, p);
-  return hipGetLastError();
+  return p.alpha_k ? launch_i8_halo_pc<WK, WP, FK, FP, R, S, NS, HJ, true>(x, w, y, p, grid, s)
+                   : launch_i8_halo_pc<WK, WP, FK, FP, R, S, NS, HJ, false>(x, w, y, p, grid, s);
 }
 
 #define I8_HALO_CFG(WK, WP, FK, FP, R, S, NS, HJ)                                     \

@@ -23,7 +23,7 @@
 
 namespace convfprop {
 
-template <int FP>
+template <int FP, bool PC>
 __global__ void __launch_bounds__(64)
 conv_i8_small_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ w,
                      int8_t *__restrict__ y, I8Params p) {
@@ -102,19 +102,26 @@ conv_i8_small_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ w,
     }
   }
 
-  store_i8_tile<1, FP>(acc, y, p, m0, ktile, lane);
+  store_i8_tile<PC, 1, FP>(acc, y, p, m0, ktile, lane);
+}
+
+template <int FP, bool PC>
+static hipError_t launch_i8_small_pc(const int8_t *x, const int8_t *w, int8_t *y, const I8Params &p,
+                                     int grid, hipStream_t s) {
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void *>(&conv_i8_small_kernel<FP, PC>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL((conv_i8_small_kernel<FP, PC>), dim3(grid), dim3(64), p.lds_bytes, s, x, w, y,
+                     p);
+  return hipGetLastError();
 }
 
 template <int FP>
 static hipError_t launch_i8_small(const int8_t *x, const int8_t *w, int8_t *y, const I8Params &p,
                                   int grid, hipStream_t s) {
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void *>(&conv_i8_small_kernel<FP>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-  if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((conv_i8_small_kernel<FP>), dim3(grid), dim3(64), p.lds_bytes, s, x, w, y,
-                     p);
-  return hipGetLastError();
+  return p.alpha_k ? launch_i8_small_pc<FP, true>(x, w, y, p, grid, s)
+                   : launch_i8_small_pc<FP, false>(x, w, y, p, grid, s);
 }
 
 #define I8_SMALL_CFG(FP)                                                            \

@@ -9,6 +9,13 @@
 //   r = rint(g)    (round half to even)
 //   y = clamp(r, -128, 127)
 // The caller guarantees a finite alpha (the C ABI rejects others).
+//
+// Per-output-channel variant (the "rowwise scaled" operators named in the
+// review thread of torchao issue 1406): a scale alpha[k] and a bias bias[k]
+// for output channel k, applied as
+//   y = clamp(rint(fl32(fl32(fl32(acc) * alpha[k]) + bias[k])), -128, 127)
+// (one fp32 multiply, then one fp32 add).  The kernels take it as a
+// compile-time flag PC, so the scalar path carries none of its code.
 #pragma once
 
 #include "common.hpp"
@@ -27,6 +34,15 @@ __device__ __forceinline__ uint32_t i8_epilogue_bits(int acc, float alpha) {
   const float f = (float)acc;
   const float g = f * alpha;
   const float c = __builtin_amdgcn_fmed3f(g, -128.0f, 127.0f);
+  return __builtin_bit_cast(uint32_t, c + 12582912.0f);
+}
+
+// The per-output-channel variant: one multiply, then one add, then as above.
+__device__ __forceinline__ uint32_t i8_epilogue_bits(int acc, float alpha, float bias) {
+  const float f = (float)acc;
+  const float g = f * alpha;
+  const float h = g + bias;
+  const float c = __builtin_amdgcn_fmed3f(h, -128.0f, 127.0f);
   return __builtin_bit_cast(uint32_t, c + 12582912.0f);
 }
 
@@ -60,14 +76,35 @@ __device__ __forceinline__ uint32_t i8_pixel_yoff(const I8Params &p, int m, int 
 // the lane's pixel; the store goes through a buffer descriptor over y, so
 // pixels past M and blocks past K/32 (offset OOB_OFFSET) are dropped
 // without a branch.
+template <bool PC>
 __device__ __forceinline__ void store_i8_frag(const v16i &v, __amdgpu_buffer_rsrc_t yr,
                                               uint32_t yoff, int kb, const I8Params &p) {
-  const float alpha = p.alpha;
   uint32_t d[4];
+  if constexpr (PC) {
+    // register 4g + j of this lane holds output channel kb*32 + 8g + 4*half + j
+    const int K4 = p.KBLK * 32 * 4;  // bytes of a per-channel array; blocks past it read 0
+    const __amdgpu_buffer_rsrc_t ar = make_rsrc(p.alpha_k, K4);
+    const __amdgpu_buffer_rsrc_t br = make_rsrc(p.bias_k, p.bias_k ? K4 : 0);
+    const uint32_t base = (uint32_t)((kb * 32 + 4 * (__lane_id() >> 5)) * 4);
+    v4f al[4], bi[4];
 #pragma unroll
-  for (int g = 0; g < 4; ++g)
-    d[g] = pack_low_bytes(i8_epilogue_bits(v[4 * g + 0], alpha), i8_epilogue_bits(v[4 * g + 1], alpha),
-                          i8_epilogue_bits(v[4 * g + 2], alpha), i8_epilogue_bits(v[4 * g + 3], alpha));
+    for (int g = 0; g < 4; ++g) {
+      al[g] = __builtin_bit_cast(v4f, load_b128(ar, base + 32 * g));
+      bi[g] = __builtin_bit_cast(v4f, load_b128(br, base + 32 * g));
+    }
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      d[g] = pack_low_bytes(i8_epilogue_bits(v[4 * g + 0], al[g][0], bi[g][0]),
+                            i8_epilogue_bits(v[4 * g + 1], al[g][1], bi[g][1]),
+                            i8_epilogue_bits(v[4 * g + 2], al[g][2], bi[g][2]),
+                            i8_epilogue_bits(v[4 * g + 3], al[g][3], bi[g][3]));
+  } else {
+    const float alpha = p.alpha;
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      d[g] = pack_low_bytes(i8_epilogue_bits(v[4 * g + 0], alpha), i8_epilogue_bits(v[4 * g + 1], alpha),
+                            i8_epilogue_bits(v[4 * g + 2], alpha), i8_epilogue_bits(v[4 * g + 3], alpha));
+  }
   // (upper half of d0) <-> (lower half of d2), likewise d1 / d3
   const auto s02 = __builtin_amdgcn_permlane32_swap(d[0], d[2], false, false);
   const auto s13 = __builtin_amdgcn_permlane32_swap(d[1], d[3], false, false);
@@ -78,7 +115,7 @@ __device__ __forceinline__ void store_i8_frag(const v16i &v, __amdgpu_buffer_rsr
 
 // An FK x FP grid of tiles: fragment (a, b) covers channel block kb_base + a
 // and pixels m_base + 32*b ...
-template <int FK, int FP>
+template <bool PC, int FK, int FP>
 __device__ __forceinline__ void store_i8_tile(const v16i (&acc)[FK][FP], int8_t *__restrict__ y,
                                               const I8Params &p, int m_base, int kb_base,
                                               int lane) {
@@ -87,7 +124,7 @@ __device__ __forceinline__ void store_i8_tile(const v16i (&acc)[FK][FP], int8_t 
   for (int b = 0; b < FP; ++b) {
     const uint32_t yoff = i8_pixel_yoff(p, m_base + 32 * b + (lane & 31), lane >> 5);
 #pragma unroll
-    for (int a = 0; a < FK; ++a) store_i8_frag(acc[a][b], yr, yoff, kb_base + a, p);
+    for (int a = 0; a < FK; ++a) store_i8_frag<PC>(acc[a][b], yr, yoff, kb_base + a, p);
   }
 }
 

@@ -21,6 +21,9 @@ struct I8Params {
   int k_tiles;  // workgroup tiles along K
   uint32_t x_bytes, w_bytes, y_bytes;
   float alpha;
+  // Per-output-channel scale and bias (device arrays of K floats), or null:
+  // then every channel uses alpha and no bias.
+  const float *alpha_k, *bias_k;
   // Halo kernel only (see conv_i8_halo.hip): virtual rows per image, halo
   // columns, halo DMA blocks per half-plane, LDS bytes per stage and total.
   int N, HV, WV;
@@ -72,6 +75,7 @@ struct F32Params {
   int k_tiles;
   uint32_t x_bytes, w_bytes;
   float alpha;
+  const float *alpha_k, *bias_k;  // per-output-channel scale and bias, or null
 };
 
 typedef hipError_t (*F32LaunchFn)(const float *x, const float *w, float *y,

@@ -124,6 +124,22 @@ conv_status_t conv2d_fprop_run(conv2d_fprop_desc_t desc, const void *x,
                                const void *w, void *y, float alpha,
                                hipStream_t stream);
 
+/* Enqueue one convolution with a scale and a bias per output channel (the
+ * "rowwise scaled" operators named in the review thread of torchao issue
+ * 1406, read as one scale and one bias per GEMM column = output channel):
+ *   int8: y = clamp(rint(fl32(fl32(fl32(acc) * alpha[k]) + bias[k])), -128, 127)
+ *   fp32: y = fl32(alpha[k] * acc) + bias[k]
+ * (one multiply, then one add; never a fused multiply-add).
+ *   alpha  device array of K floats (required)
+ *   bias   device array of K floats, or NULL for no bias
+ * x, w, y as for conv2d_fprop_run.  alpha and bias must be 16-byte aligned
+ * and must not overlap y.  The values are read on the device, so they are
+ * not checked: a non-finite alpha[k] or bias[k] gives unspecified int8
+ * values in channel k (never a fault). */
+conv_status_t conv2d_fprop_run_scaled(conv2d_fprop_desc_t desc, const void *x,
+                                      const void *w, void *y, const float *alpha,
+                                      const float *bias, hipStream_t stream);
+
 /* Layout transforms (pure permutations, int8).  C must be a multiple of 32.
  * src and dst must not overlap; both 16-byte aligned.
  *   NCHW [N][C][H][W]          <-> NCxHWx<32> [N][C/32][H][W][32]

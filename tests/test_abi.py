@@ -154,6 +154,23 @@ def test_run_rejects_null_and_misaligned_before_launch(b):
     b.lib.conv2d_fprop_desc_destroy(h)
 
 
+def test_run_scaled_rejects_bad_arguments_before_launch(b):
+    st, h = _create(b, 1, 32, 8, 8, 32, 3, 3, 1, 1, 1, 1, 1, 1)
+    assert st == 0
+    run = b.lib.conv2d_fprop_run_scaled
+    x, w, y, a, bias = 4096, 1 << 16, 1 << 20, 1 << 24, (1 << 24) + 4096
+    assert run(h, x, w, y, 0, bias, None) == b.CONV_ERR_NULL          # alpha required
+    assert run(h, 0, w, y, a, bias, None) == b.CONV_ERR_NULL
+    assert run(None, x, w, y, a, bias, None) == b.CONV_ERR_NULL
+    assert run(h, x, w, y, a + 4, bias, None) == b.CONV_ERR_MISALIGNED  # 16-byte alignment
+    assert run(h, x, w, y, a, bias + 8, None) == b.CONV_ERR_MISALIGNED
+    assert run(h, x + 1, w, y, a, bias, None) == b.CONV_ERR_MISALIGNED
+    # the per-channel arrays (32 floats) must not overlap y (2 KiB at 1 MiB)
+    assert run(h, x, w, y, y + 512, bias, None) == b.CONV_ERR_UNSUPPORTED
+    assert run(h, x, w, y, a, y + 1024, None) == b.CONV_ERR_UNSUPPORTED
+    b.lib.conv2d_fprop_desc_destroy(h)
+
+
 def test_transforms_reject_bad_arguments(b):
     f = b.lib.conv_nchw_to_nc32hw32_i8
     assert f(0, 4096, 1, 32, 2, 2, None) == b.CONV_ERR_NULL

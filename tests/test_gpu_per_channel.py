@@ -1,0 +1,155 @@
+"""GPU parity of the per-output-channel scale and bias entry point
+(conv2d_fprop_run_scaled) against the oracle's per-channel epilogue.
+
+int8: bit-exact, every compiled configuration on ragged shapes, and the full
+3x3 N32 C256 workload.  fp32: the tolerance rule of the other fp32 tests, and
+exact equality on integer-valued inputs with dyadic scales and biases.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from convolution_forward_gemm_amd import workloads as wl
+from test_gpu_parity import (NTHREADS, ConfigNotApplicable, _announce, _b, _dev,
+                             assert_f32_rule, each_config)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _scales(K, seed, scale):
+    """alpha[k] = scale * U[0.5, 2), bias[k] = U[-3, 3) as float32 (seeded)."""
+    r = wl.rng(31, seed, K)
+    alpha = (scale * r.uniform(0.5, 2.0, K)).astype(np.float32)
+    bias = r.uniform(-3.0, 3.0, K).astype(np.float32)
+    return alpha, bias
+
+
+def gpu_conv_i8_scaled(x, w, alpha, bias, pad, stride, dil, config=None):
+    b = _b()
+    N, C, H, W = x.shape
+    K, _, R, S = w.shape
+    conv = b.Conv2dFprop(N, C, H, W, K, R, S, pad=pad, stride=stride, dil=dil, dtype="int8")
+    if config is not None:
+        try:
+            conv.set_config(config)
+        except b.ConvError as e:
+            if e.status != b.CONV_ERR_UNSUPPORTED:
+                raise
+            raise ConfigNotApplicable(str(e))
+    x_il = b.nchw_to_nc32hw32(_dev(x))
+    w_il = b.kcrs_to_c32rsk32(_dev(w))
+    y = torch.full(conv.y_shape, 77, dtype=torch.int8, device="cuda")  # poison
+    conv.run_scaled(x_il, w_il, _dev(alpha), _dev(bias) if bias is not None else None, y)
+    torch.cuda.synchronize()
+    return y.cpu().numpy(), conv
+
+
+CASES = [
+    # N, C, H, W, K, R, S, pad, stride, dil
+    (2, 64, 13, 11, 96, 3, 3, (1, 1), (1, 1), (1, 1)),
+    (2, 256, 9, 7, 320, 3, 3, (1, 1), (1, 1), (1, 1)),     # ragged K tile
+    (3, 64, 23, 21, 96, 3, 3, (1, 1), (2, 2), (1, 1)),     # stride 2
+    (3, 96, 7, 7, 32, 1, 1, (0, 0), (1, 1), (1, 1)),       # 1x1
+]
+
+
+@pytest.mark.parametrize("case", CASES)
+@pytest.mark.parametrize("with_bias", [True, False])
+def test_int8_per_channel_configs(case, with_bias):
+    N, C, H, W, K, R, S, pad, stride, dil = case
+    x = wl.int8_uniform((N, C, H, W), -128, 127, 32, *case[:7])
+    w = wl.int8_uniform((K, C, R, S), -128, 127, 33, *case[:7])
+    alpha, bias = _scales(K, 1, 2.0 ** -11)
+    if not with_bias:
+        bias = None
+    _, ref = oracle.conv2d_i8_scaled(x, w, alpha, bias, pad=pad, stride=stride, dil=dil,
+                                     nthreads=NTHREADS)
+    ref_il = oracle.nchw_to_nc32hw32(ref)
+
+    def run(cfg):
+        _announce("int8 per-channel", case, "bias", with_bias, "config", cfg)
+        y, conv = gpu_conv_i8_scaled(x, w, alpha, bias, pad, stride, dil, config=cfg)
+        assert np.array_equal(y, ref_il), conv.config
+    each_config("int8", run)
+
+
+def test_int8_per_channel_workload_c3():
+    wk = wl.WORKLOADS["c3"]
+    x, w = wl.make_inputs(wk)
+    alpha, bias = _scales(wk.K, 2, wk.alpha)
+    _announce("int8 per-channel full", wk.key)
+    y, _ = gpu_conv_i8_scaled(x, w, alpha, bias, wk.pad, wk.stride, wk.dil)
+    _, ref = oracle.conv2d_i8_scaled(x, w, alpha, bias, nthreads=NTHREADS, **wk.conv_kwargs)
+    assert np.array_equal(y, oracle.nchw_to_nc32hw32(ref))
+
+
+def test_int8_one_scale_matches_the_scalar_entry_point():
+    # alpha[k] = alpha for every k and no bias: the same bytes as conv2d_fprop_run
+    from test_gpu_parity import gpu_conv_i8
+    case = (2, 64, 13, 11, 96, 3, 3, (1, 1), (1, 1), (1, 1))
+    N, C, H, W, K, R, S, pad, stride, dil = case
+    x = wl.int8_uniform((N, C, H, W), -128, 127, 34, *case[:7])
+    w = wl.int8_uniform((K, C, R, S), -128, 127, 35, *case[:7])
+    a = 2.0 ** -10
+    _announce("int8 per-channel vs scalar", case)
+    y1, _ = gpu_conv_i8_scaled(x, w, np.full(K, a, np.float32), None, pad, stride, dil)
+    y2, _ = gpu_conv_i8(x, w, a, pad, stride, dil)
+    assert np.array_equal(y1, y2)
+
+
+def gpu_conv_f32_scaled(x, w, alpha, bias, pad, stride, dil, config=None):
+    b = _b()
+    N, C, H, W = x.shape
+    K, _, R, S = w.shape
+    conv = b.Conv2dFprop(N, C, H, W, K, R, S, pad=pad, stride=stride, dil=dil, dtype="fp32")
+    if config is not None:
+        try:
+            conv.set_config(config)
+        except b.ConvError as e:
+            if e.status != b.CONV_ERR_UNSUPPORTED:
+                raise
+            raise ConfigNotApplicable(str(e))
+    y = torch.full(conv.y_shape, float("nan"), dtype=torch.float32, device="cuda")
+    conv.run_scaled(_dev(x), _dev(w), _dev(alpha), _dev(bias) if bias is not None else None, y)
+    torch.cuda.synchronize()
+    return y.cpu().numpy(), conv
+
+
+F32_CASES = [
+    (2, 5, 13, 11, 40, 3, 3, (1, 1), (1, 1), (1, 1)),
+    (1, 32, 20, 24, 64, 5, 9, (2, 4), (1, 1), (2, 3)),
+]
+
+
+@pytest.mark.parametrize("case", F32_CASES)
+def test_f32_per_channel_configs(case):
+    N, C, H, W, K, R, S, pad, stride, dil = case
+    x, w = wl.make_custom("fp32", N, C, H, W, K, R, S, seed=7)
+    alpha, bias = _scales(K, 3, 1.0)
+    acc = oracle.conv2d_f32_acc(x, w, pad=pad, stride=stride, dil=dil, nthreads=NTHREADS)
+    ref = oracle.epilogue_f32_per_channel(acc, alpha, bias)
+
+    def run(cfg):
+        _announce("fp32 per-channel", case, "config", cfg)
+        y, _ = gpu_conv_f32_scaled(x, w, alpha, bias, pad, stride, dil, config=cfg)
+        assert_f32_rule(y, ref)
+    each_config("fp32", run)
+
+
+def test_f32_per_channel_integer_valued_exact():
+    # x, w in {-1, 0, 1}: every partial sum is an exact small integer; dyadic
+    # scales and biases keep alpha[k]*acc + bias[k] exact in fp32
+    case = (2, 16, 11, 9, 48, 3, 3, (1, 1), (1, 1), (1, 1))
+    N, C, H, W, K, R, S, pad, stride, dil = case
+    r = wl.rng(36, *case[:7])
+    x = r.integers(-1, 2, size=(N, C, H, W)).astype(np.float32)
+    w = r.integers(-1, 2, size=(K, C, R, S)).astype(np.float32)
+    alpha = np.array([2.0 ** -(k % 5) for k in range(K)], np.float32)
+    bias = np.array([(k % 7) * 0.25 - 1.0 for k in range(K)], np.float32)
+    acc = oracle.conv2d_f32_acc(x, w, pad=pad, stride=stride, dil=dil)
+    ref = oracle.epilogue_f32_per_channel(acc, alpha, bias)
+    _announce("fp32 per-channel exact", case)
+    y, _ = gpu_conv_f32_scaled(x, w, alpha, bias, pad, stride, dil)
+    assert np.array_equal(y, ref)

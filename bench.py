@@ -110,21 +110,16 @@ def latency_suite(torch, conv, xd, wd, yd, alpha, calls=1000):
 
     graph_us = None
     try:
-        g = torch.cuda.CUDAGraph()
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
-            gstream = torch.cuda.current_stream().cuda_stream
-            conv.run_ptr(xp, wp, yp, alpha, gstream)  # warm on the side stream
-            torch.cuda.synchronize()
-            with torch.cuda.graph(g, stream=s):
-                cap = torch.cuda.current_stream().cuda_stream
-                for _ in range(20):
-                    conv.run_ptr(xp, wp, yp, alpha, cap)
+        # the library's own capture of 20 back-to-back calls
+        # (conv2d_fprop_graph_create), replayed on the current stream
+        from convolution_forward_gemm_amd import binding as b
+        g = b.ConvGraph(conv, xp, wp, yp, alpha, 20)
+        g.launch(stream)
         torch.cuda.synchronize()
         reps = 50
-        ms = time_device(torch, g.replay, reps, 5)
+        ms = time_device(torch, lambda: g.launch(stream), reps, 5)
         graph_us = ms * 1e3 / 20
+        del g
     except Exception as e:  # graph capture is a secondary measurement
         graph_us = "unavailable: %s" % (type(e).__name__,)
     return {"device_us_per_call": round(dev_ms * 1e3, 3),

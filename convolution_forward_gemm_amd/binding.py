@@ -50,6 +50,9 @@ SIGNATURES = {
     "conv2d_fprop_desc_set_config": (_i, [_p, _i]),
     "conv2d_fprop_run": (_i, [_p, _p, _p, _p, _f, _p]),
     "conv2d_fprop_run_scaled": (_i, [_p, _p, _p, _p, _p, _p, _p]),
+    "conv2d_fprop_graph_create": (_i, [ctypes.POINTER(_p), _p, _p, _p, _p, _f, _i]),
+    "conv2d_fprop_graph_launch": (_i, [_p, _p]),
+    "conv2d_fprop_graph_destroy": (_i, [_p]),
     "conv_nchw_to_nc32hw32_i8": (_i, [_p, _p, _i, _i, _i, _i, _p]),
     "conv_nc32hw32_to_nchw_i8": (_i, [_p, _p, _i, _i, _i, _i, _p]),
     "conv_kcrs_to_c32rsk32_i8": (_i, [_p, _p, _i, _i, _i, _i, _p]),
@@ -204,6 +207,29 @@ class Conv2dFprop:
         self.run_ptr(x.data_ptr(), w.data_ptr(), y.data_ptr(), float(alpha),
                      _stream_handle(stream))
         return y
+
+
+class ConvGraph:
+    """`calls` back-to-back runs of a descriptor on fixed device buffers,
+    captured once into a HIP graph by the library; launch() replays them."""
+
+    def __init__(self, conv: "Conv2dFprop", x_ptr: int, w_ptr: int, y_ptr: int, alpha: float,
+                 calls: int):
+        self._h = None
+        h = _p()
+        _check(lib.conv2d_fprop_graph_create(ctypes.byref(h), conv._h, x_ptr, w_ptr, y_ptr,
+                                             alpha, calls), "conv2d_fprop_graph_create")
+        self._h = h
+        self._conv = conv  # the descriptor outlives the graph
+        self.calls = calls
+
+    def launch(self, stream_handle: int = 0):
+        _check(lib.conv2d_fprop_graph_launch(self._h, stream_handle), "conv2d_fprop_graph_launch")
+
+    def __del__(self):
+        if getattr(self, "_h", None) is not None and lib is not None:
+            lib.conv2d_fprop_graph_destroy(self._h)
+            self._h = None
 
 
 def _prod(shape):

@@ -449,6 +449,59 @@ conv_status_t conv2d_fprop_run_scaled(conv2d_fprop_desc_t d, const void *x, cons
   return run_impl(d, x, w, y, 1.0f, alpha, bias, stream);
 }
 
+// ---- graph capture of repeated runs ----------------------------------------
+struct conv2d_fprop_graph_s {
+  hipGraphExec_t exec = nullptr;
+};
+
+conv_status_t conv2d_fprop_graph_create(conv2d_fprop_graph_t *out, conv2d_fprop_desc_t d,
+                                        const void *x, const void *w, void *y, float alpha,
+                                        int calls) {
+  if (!out) return CONV_ERR_NULL;
+  *out = nullptr;
+  conv_status_t st = check_run(d, x, w, y);
+  if (st != CONV_OK) return st;
+  if (d->dtype == CONV_DTYPE_INT8 && !isfinite(alpha)) return CONV_ERR_INVALID_ALPHA;
+  if (calls < 1 || calls > 4096) return CONV_ERR_INVALID_SHAPE;
+  conv2d_fprop_graph_s *g = new (std::nothrow) conv2d_fprop_graph_s();
+  if (!g) return CONV_ERR_NO_MEMORY;
+  // capture on a private stream, so the caller's streams are untouched
+  hipStream_t s = nullptr;
+  hipGraph_t graph = nullptr;
+  st = CONV_ERR_HIP;
+  if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) == hipSuccess) {
+    if (hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal) == hipSuccess) {
+      conv_status_t rs = CONV_OK;
+      for (int i = 0; i < calls && rs == CONV_OK; ++i)
+        rs = run_impl(d, x, w, y, alpha, nullptr, nullptr, s);
+      const hipError_t ec = hipStreamEndCapture(s, &graph);
+      if (rs == CONV_OK && ec == hipSuccess &&
+          hipGraphInstantiate(&g->exec, graph, nullptr, nullptr, 0) == hipSuccess)
+        st = CONV_OK;
+      if (graph) (void)hipGraphDestroy(graph);
+    }
+    (void)hipStreamDestroy(s);
+  }
+  if (st != CONV_OK) {
+    delete g;
+    return st;
+  }
+  *out = g;
+  return CONV_OK;
+}
+
+conv_status_t conv2d_fprop_graph_launch(conv2d_fprop_graph_t g, hipStream_t stream) {
+  if (!g) return CONV_ERR_NULL;
+  return hipGraphLaunch(g->exec, stream) == hipSuccess ? CONV_OK : CONV_ERR_HIP;
+}
+
+conv_status_t conv2d_fprop_graph_destroy(conv2d_fprop_graph_t g) {
+  if (!g) return CONV_OK;
+  const hipError_t e = hipGraphExecDestroy(g->exec);
+  delete g;
+  return e == hipSuccess ? CONV_OK : CONV_ERR_HIP;
+}
+
 // ---- layout transforms ----------------------------------------------------
 static conv_status_t check_transform(const int8_t *src, int8_t *dst, int a, int C, int b,
                                      int c) {

@@ -140,6 +140,25 @@ conv_status_t conv2d_fprop_run_scaled(conv2d_fprop_desc_t desc, const void *x,
                                       const void *w, void *y, const float *alpha,
                                       const float *bias, hipStream_t stream);
 
+/* Repeated runs as one HIP graph (the "CUDA Graphs" section of the CUTLASS
+ * host-latency notes): `calls` back-to-back runs of `desc` on the fixed
+ * buffers x, w, y with scale alpha are captured once, on a private stream,
+ * and instantiated; each launch then enqueues all of them on `stream` with
+ * one call and no per-kernel host work.  Creation is a setup step (it
+ * creates and destroys a stream, and the runtime allocates the graph's
+ * resources); launch only enqueues.  The buffers must stay valid for the
+ * graph's lifetime.  1 <= calls <= 4096; the argument checks and errors are
+ * those of conv2d_fprop_run.  Destroy with conv2d_fprop_graph_destroy (NULL
+ * is accepted). */
+typedef struct conv2d_fprop_graph_s *conv2d_fprop_graph_t;
+conv_status_t conv2d_fprop_graph_create(conv2d_fprop_graph_t *out,
+                                        conv2d_fprop_desc_t desc, const void *x,
+                                        const void *w, void *y, float alpha,
+                                        int calls);
+conv_status_t conv2d_fprop_graph_launch(conv2d_fprop_graph_t graph,
+                                        hipStream_t stream);
+conv_status_t conv2d_fprop_graph_destroy(conv2d_fprop_graph_t graph);
+
 /* Layout transforms (pure permutations, int8).  C must be a multiple of 32.
  * src and dst must not overlap; both 16-byte aligned.
  *   NCHW [N][C][H][W]          <-> NCxHWx<32> [N][C/32][H][W][32]

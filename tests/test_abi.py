@@ -171,6 +171,24 @@ def test_run_scaled_rejects_bad_arguments_before_launch(b):
     b.lib.conv2d_fprop_desc_destroy(h)
 
 
+def test_graph_create_rejects_bad_arguments_before_capture(b):
+    st, h = _create(b, 1, 32, 8, 8, 32, 3, 3, 1, 1, 1, 1, 1, 1)
+    assert st == 0
+    g = ctypes.c_void_p()
+    create = b.lib.conv2d_fprop_graph_create
+    x, w, y = 4096, 1 << 16, 1 << 20
+    assert create(None, h, x, w, y, 1.0, 4) == b.CONV_ERR_NULL
+    assert create(ctypes.byref(g), None, x, w, y, 1.0, 4) == b.CONV_ERR_NULL
+    assert create(ctypes.byref(g), h, x + 1, w, y, 1.0, 4) == b.CONV_ERR_MISALIGNED
+    assert create(ctypes.byref(g), h, x, w, y, float("nan"), 4) == b.CONV_ERR_INVALID_ALPHA
+    for calls in (0, -1, 4097):
+        assert create(ctypes.byref(g), h, x, w, y, 1.0, calls) == b.CONV_ERR_INVALID_SHAPE
+    assert not g.value
+    assert b.lib.conv2d_fprop_graph_launch(None, None) == b.CONV_ERR_NULL
+    assert b.lib.conv2d_fprop_graph_destroy(None) == b.CONV_OK
+    b.lib.conv2d_fprop_desc_destroy(h)
+
+
 def test_transforms_reject_bad_arguments(b):
     f = b.lib.conv_nchw_to_nc32hw32_i8
     assert f(0, 4096, 1, 32, 2, 2, None) == b.CONV_ERR_NULL

@@ -452,6 +452,7 @@ def main():
         c2, x2, w2d, y2, _ = setup(w2, torch, b)
         lat2 = latency_suite(torch, c2, x2, w2d, y2, w2.alpha)
         lat2["config"] = c2.config
+        lat2["GBps_device"] = round(conv_bytes(w2, c2.P, c2.Q, 1) / (lat2["device_us_per_call"] * 1e-6) / 1e9, 3)
         extra["c2_1x1_us_per_call"] = lat2
         # strided 3x3
         w4 = wl.WORKLOADS["c4"]
@@ -484,6 +485,25 @@ def main():
         extra["transform_nchw_to_nc32hw32_c3x"] = {"ms": round(mst, 6),
                                                    "GBps": round(2 * xs.numel() / (mst * 1e-3) / 1e9, 1)}
         del xs, ilb
+        # one GPU's share under the sharding plan (design only here): the
+        # 3x3 C256 workload split 8 ways over the batch (N = 4 per GPU), and
+        # the dilated fp32 one split 8 ways over output rows (64 rows per GPU
+        # read 72 input rows, halo included); configurations from the
+        # selection model, not the per-shape table
+        shard = {}
+        for key, swk in (
+                ("c3_batch_shard_n4", wl.Workload("c3n4", "", "int8", 4, 256, 28, 28, 256, 3, 3, (1, 1),
+                                                  (1, 1), (1, 1), -128, 127, 2.0 ** -14, 2)),
+                ("c5_row_shard_72x512", wl.Workload("c5h", "", "fp32", 8, 32, 72, 512, 64, 5, 9, (0, 4),
+                                                    (1, 1), (2, 3), 0, 0, 1.0, 4))):
+            cs, xs_, ws_, ys_, _ = setup(swk, torch, b)
+            n_it = 2000 if swk.dtype == "int8" else 50
+            mss_ = time_device(torch, lambda: cs.run_ptr(xs_.data_ptr(), ws_.data_ptr(), ys_.data_ptr(),
+                                                         swk.alpha, s4), n_it, n_it // 2)
+            tt = conv_ops(swk, cs.P, cs.Q) / (mss_ * 1e-3) / 1e12
+            shard[key] = {"us": round(mss_ * 1e3, 3), "T_ops_per_s": round(tt, 3), "config": cs.config}
+            del cs, xs_, ws_, ys_
+        extra["one_gpu_share_of_sharded_workloads"] = shard
         # fp32 dilated
         w5 = wl.WORKLOADS["c5"]
         c5, x5, w5d, y5, _ = setup(w5, torch, b)

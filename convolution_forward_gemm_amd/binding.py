@@ -127,7 +127,7 @@ class Conv2dFprop:
 
     def __del__(self):
         h = getattr(self, "_h", None)
-        if h is not None and h.value:
+        if h is not None and h.value and lib is not None:  # lib is None at interpreter exit
             lib.conv2d_fprop_desc_destroy(h)
             self._h = None
 

@@ -136,6 +136,24 @@ const char *const kI8SmallCandidates[] = {
     "i8_mfma32x32x32_wg1x1_frag1x1_kt2_ring4_rsouter_false",
 };
 
+// Configuration-selection model for shapes without a table entry, fitted to
+// shape-grid sweeps (fit_select.py): per configuration, its workgroups per
+// CU and the coefficients k[0..6] of its predicted time
+//   t_us = k0 + R * (k1 + k2 * W + k3 * L + k4 * C / 100 + k5 * Rf * Sf / 10)
+//          + k6 * grid * W / 1000,
+//   R = ceil(grid / (256 * occupancy)) (rounds of workgroups), W = bm * bn *
+//   C * Rf * Sf / 1e6 (a tile's multiply-adds), L = C * Rf * Sf / 1e3.
+struct SelectModel {
+  conv_dtype_t dtype;
+  const char *name;
+  int occ;
+  float k[7];
+};
+const SelectModel kSelectModel[] = {
+#include "select_model.inc"
+    {CONV_DTYPE_INT8, nullptr, 0, {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}},  // end of table
+};
+
 int f32_lds_bytes(const conv2d_fprop_desc_s &d, int cfg) {
   return kF32Configs[cfg].lds_bytes * d.R * d.S;
 }
@@ -259,6 +277,58 @@ bool plan(conv2d_fprop_desc_s &d, int cfg) {
   return true;
 }
 
+// Dynamic LDS bytes and threads of one workgroup of the planned launch.
+int desc_lds_bytes(const conv2d_fprop_desc_s &d) {
+  return d.dtype == CONV_DTYPE_INT8 ? d.i8.lds_bytes : f32_lds_bytes(d, d.config);
+}
+int desc_threads(const conv2d_fprop_desc_s &d) {
+  return d.dtype == CONV_DTYPE_INT8 ? i8_config(d.config)->threads : kF32Configs[d.config].threads;
+}
+
+const char *config_name(conv_dtype_t dtype, int cfg) {
+  return dtype == CONV_DTYPE_INT8 ? i8_config(cfg)->name : kF32Configs[cfg].name;
+}
+
+// Predicted microseconds of a planned descriptor under its configuration's
+// model entry; negative if the configuration has none.
+double select_time(const conv2d_fprop_desc_s &d) {
+  const char *name = config_name(d.dtype, d.config);
+  for (const SelectModel &m : kSelectModel) {
+    if (!m.name || m.dtype != d.dtype || strcmp(m.name, name) != 0) continue;
+    const int lds = desc_lds_bytes(d), threads = desc_threads(d);
+    int occ = m.occ;
+    if (lds > 0 && 163840 / lds < occ) occ = 163840 / lds;
+    const int tlim = 2048 / threads > 1 ? 2048 / threads : 1;
+    if (tlim < occ) occ = tlim;
+    if (occ < 1) occ = 1;
+    const int bm = d.dtype == CONV_DTYPE_INT8 ? i8_config(d.config)->bm : kF32Configs[d.config].bm;
+    const int bn = d.dtype == CONV_DTYPE_INT8 ? i8_config(d.config)->bn : kF32Configs[d.config].bn;
+    const double R = (double)((d.grid + 256 * occ - 1) / (256 * occ));
+    const double crs = (double)d.C * d.R * d.S;
+    const double W = (double)bm * bn * crs / 1e6, L = crs / 1e3;
+    return m.k[0] +
+           R * (m.k[1] + m.k[2] * W + m.k[3] * L + m.k[4] * d.C / 100.0 + m.k[5] * d.R * d.S / 10.0) +
+           m.k[6] * d.grid * W / 1000.0;
+  }
+  return -1.0;
+}
+
+// The configuration with the least predicted time among those that plan for
+// the problem (earlier configurations win ties); false if none has a model.
+bool plan_by_model(conv2d_fprop_desc_s &d) {
+  const int n = d.dtype == CONV_DTYPE_INT8 ? num_i8_configs() : kNumF32Configs;
+  int best = -1;
+  double best_t = 0.0;
+  for (int c = 0; c < n; ++c) {
+    conv2d_fprop_desc_s trial = d;
+    if (!plan(trial, c)) continue;
+    const double t = select_time(trial);
+    if (t < 0.0) continue;
+    if (best < 0 || t < best_t) best = c, best_t = t;
+  }
+  return best >= 0 && plan(d, best);
+}
+
 }  // namespace
 
 extern "C" {
@@ -324,6 +394,7 @@ conv_status_t conv2d_fprop_desc_create(conv2d_fprop_desc_t *out, int N, int C,
   bool ok = false;
   const int cfg = lookup_shape(*d);
   if (cfg >= 0) ok = plan(*d, cfg);
+  if (!ok) ok = plan_by_model(*d);
   if (!ok && dtype == CONV_DTYPE_INT8) {
     // Among the candidates that plan, the least estimated time: rounds of
     // workgroups over the 256 CUs times the MFMA work of one tile (earlier
@@ -376,8 +447,8 @@ conv_status_t conv2d_fprop_desc_get_config(conv2d_fprop_desc_t d, char *buf, siz
   const char *name = i8 ? i8_config(d->config)->name : kF32Configs[d->config].name;
   const int bm = i8 ? i8_config(d->config)->bm : kF32Configs[d->config].bm;
   const int bn = i8 ? i8_config(d->config)->bn : kF32Configs[d->config].bn;
-  snprintf(buf, n, "config=%d %s tile=%dch x %dpx grid=%d", d->config, name, bm, bn,
-           d->grid);
+  snprintf(buf, n, "config=%d %s tile=%dch x %dpx grid=%d lds=%d threads=%d", d->config, name,
+           bm, bn, d->grid, desc_lds_bytes(*d), desc_threads(*d));
   return CONV_OK;
 }
 

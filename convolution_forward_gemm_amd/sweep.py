@@ -220,6 +220,156 @@ def summarize_trace(key, trace_dir, command, out_dir, sweep_log=None):
     return path
 
 
+# ---------------------------------------------------------------------------
+# Shape grids for the configuration-selection model (fit_select.py): every
+# configuration that runs each shape, timed back to back on resident
+# synthetic operands.  "train" fits the model, "validate" (held-out shapes,
+# seeded random plus the per-GPU shares of the sharding plan) checks it.
+# A shape is (dtype, N, C, H, W, K, R, S, ph, pw, sh, sw, dh, dw).
+# ---------------------------------------------------------------------------
+_FILTERS_I8 = ((1, 1, 0, 0, 1, 1, 1, 1), (3, 3, 1, 1, 1, 1, 1, 1), (3, 3, 1, 1, 2, 2, 1, 1),
+               (5, 5, 2, 2, 1, 1, 1, 1), (3, 3, 2, 2, 1, 1, 2, 2), (7, 7, 3, 3, 2, 2, 1, 1))
+_FILTERS_F32 = ((3, 3, 1, 1, 1, 1, 1, 1), (5, 9, 2, 4, 1, 1, 2, 3), (1, 1, 0, 0, 1, 1, 1, 1),
+                (5, 5, 2, 2, 2, 2, 1, 1))
+
+
+def _out_dim(x, pad, dil, k, st):
+    return (x + 2 * pad - dil * (k - 1) - 1) // st + 1
+
+
+def _shape_ok(sh, max_elems=1 << 26, max_ops=2.5e11):
+    dt, N, C, H, W, K, R, S, ph, pw, sth, stw, dh, dw = sh
+    P, Q = _out_dim(H, ph, dh, R, sth), _out_dim(W, pw, dw, S, stw)
+    if P < 1 or Q < 1:
+        return False
+    ops = 2.0 * N * K * P * Q * C * R * S
+    return N * C * H * W <= max_elems and N * K * P * Q <= max_elems and ops <= max_ops
+
+
+def grid_shapes(kind):
+    import numpy as np
+    out = []
+    if kind == "train":
+        for N in (1, 4, 16, 64):
+            for C, K in ((64, 64), (128, 128), (256, 256), (512, 512), (64, 256), (256, 64)):
+                for H in (7, 14, 28, 56):
+                    for R, S, ph, pw, sh, sw, dh, dw in _FILTERS_I8[:3]:
+                        out.append(("int8", N, C, H, H, K, R, S, ph, pw, sh, sw, dh, dw))
+        for N in (2, 32):
+            for C, K in ((96, 160), (320, 192), (32, 448)):
+                for H in (9, 20, 41):
+                    for R, S, ph, pw, sh, sw, dh, dw in _FILTERS_I8[3:]:
+                        out.append(("int8", N, C, H, H, K, R, S, ph, pw, sh, sw, dh, dw))
+        for N in (1, 8):
+            for C in (3, 32, 64):
+                for K in (32, 64, 128):
+                    for H, W in ((64, 64), (256, 256), (128, 200)):
+                        for R, S, ph, pw, sh, sw, dh, dw in _FILTERS_F32:
+                            out.append(("fp32", N, C, H, W, K, R, S, ph, pw, sh, sw, dh, dw))
+    elif kind == "validate":
+        out += [("int8", 4, 256, 28, 28, 256, 3, 3, 1, 1, 1, 1, 1, 1),    # 3x3 C256 share, N/8
+                ("int8", 4, 128, 56, 56, 256, 3, 3, 1, 1, 2, 2, 1, 1),    # stride-2 share, N/8
+                ("fp32", 8, 32, 72, 512, 64, 5, 9, 0, 4, 1, 1, 2, 3)]     # dilated 5x9 share, H/8
+        rng = np.random.default_rng((2026, 77))
+        while len(out) < 3 + 30:
+            f = _FILTERS_I8[rng.integers(len(_FILTERS_I8))]
+            H = int(rng.integers(5, 61))
+            sh = ("int8", int(rng.integers(1, 49)), 32 * int(rng.integers(1, 17)), H,
+                  int(rng.choice([H, rng.integers(5, 61)])), 32 * int(rng.integers(1, 17))) + f
+            if _shape_ok(sh):
+                out.append(sh)
+        while len(out) < 3 + 30 + 10:
+            f = _FILTERS_F32[rng.integers(len(_FILTERS_F32))]
+            H = int(rng.integers(16, 300))
+            sh = ("fp32", int(rng.integers(1, 9)), int(rng.integers(1, 65)), H,
+                  int(rng.integers(16, 300)), 16 * int(rng.integers(1, 9))) + f
+            if _shape_ok(sh):
+                out.append(sh)
+    else:
+        raise ValueError(kind)
+    return [sh for sh in out if _shape_ok(sh)]
+
+
+def _parse_config(text):
+    import re
+    m = re.match(r"config=(\d+) (\S+) tile=(\d+)ch x (\d+)px grid=(\d+) lds=(\d+) threads=(\d+)", text)
+    i, name, bm, bn, grid, lds, thr = m.groups()
+    return {"config": int(i), "name": name, "bm": int(bm), "bn": int(bn), "grid": int(grid),
+            "lds": int(lds), "threads": int(thr)}
+
+
+def _median_us(torch, fn, target_us=300.0, reps=3):
+    def run(calls):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(calls):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / calls
+    t = run(2)
+    calls = int(min(200, max(3, target_us / max(t, 1e-3))))
+    ts = sorted(run(calls) for _ in range(reps))
+    return ts[len(ts) // 2]
+
+
+def run_shape_grid(kind, out_path):
+    """Time every configuration that runs each shape of the grid; one JSON
+    line per (shape, configuration) appended to out_path."""
+    import torch
+    from . import binding as b
+
+    shapes = grid_shapes(kind)
+    s = torch.cuda.current_stream().cuda_stream
+    # steady clock first: ~0.1 s of back-to-back work
+    wc = b.Conv2dFprop(32, 256, 28, 28, 256, 3, 3, pad=1)
+    xw = torch.zeros(wc.x_shape, dtype=torch.int8, device="cuda")
+    ww = torch.zeros(wc.w_shape, dtype=torch.int8, device="cuda")
+    yw = torch.empty(wc.y_shape, dtype=torch.int8, device="cuda")
+    for _ in range(6000):
+        wc.run_ptr(xw.data_ptr(), ww.data_ptr(), yw.data_ptr(), 1.0, s)
+    torch.cuda.synchronize()
+    del xw, ww, yw
+    gen = torch.Generator(device="cuda")
+    with open(out_path, "a") as f:
+        for si, sh in enumerate(shapes):
+            dt, N, C, H, W, K, R, S, ph, pw, sth, stw, dh, dw = sh
+            conv = b.Conv2dFprop(N, C, H, W, K, R, S, pad=(ph, pw), stride=(sth, stw), dil=(dh, dw),
+                                 dtype=dt)
+            default = _parse_config(conv.config)["config"]
+            gen.manual_seed(si)
+            if dt == "int8":
+                x = torch.randint(-128, 128, conv.x_shape, dtype=torch.int8, device="cuda", generator=gen)
+                w = torch.randint(-128, 128, conv.w_shape, dtype=torch.int8, device="cuda", generator=gen)
+                y = torch.empty(conv.y_shape, dtype=torch.int8, device="cuda")
+                alpha = 2.0 ** -14
+            else:
+                x = torch.randn(conv.x_shape, device="cuda", generator=gen)
+                w = torch.randn(conv.w_shape, device="cuda", generator=gen) / (C * R * S) ** 0.5
+                y = torch.empty(conv.y_shape, device="cuda")
+                alpha = 1.0
+            xp, wp, yp = x.data_ptr(), w.data_ptr(), y.data_ptr()
+            n = 0
+            for i in range(b.num_configs(dt)):
+                try:
+                    conv.set_config(i)
+                except b.ConvError as e:
+                    if e.status != b.CONV_ERR_UNSUPPORTED:
+                        raise
+                    continue
+                us = _median_us(torch, lambda: conv.run_ptr(xp, wp, yp, alpha, s))
+                rec = {"kind": kind, "shape": list(sh)}
+                rec.update(_parse_config(conv.config))
+                rec["us"] = round(us, 3)
+                rec["default"] = i == default
+                f.write(json.dumps(rec) + "\n")
+                n += 1
+            f.flush()
+            print("shape %d/%d %s: %d configurations" % (si + 1, len(shapes), sh, n), flush=True)
+            del x, w, y, conv
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--workload", default="c3")
@@ -231,7 +381,12 @@ def main():
     ap.add_argument("--sweep-log", metavar="FILE", help="with --summarize-trace: the sweep's output")
     ap.add_argument("--command", default="")
     ap.add_argument("--out-dir", default=os.path.join(ROOT, "profiles"))
+    ap.add_argument("--grid", choices=["train", "validate"], help="time a shape grid (model fit)")
+    ap.add_argument("--out", help="with --grid: JSON-lines output file")
     a = ap.parse_args()
+    if a.grid:
+        run_shape_grid(a.grid, a.out)
+        return
     if a.summarize_trace:
         print(summarize_trace(a.workload, a.summarize_trace, a.command, a.out_dir, a.sweep_log))
         return

@@ -114,28 +114,6 @@ int lookup_shape(const conv2d_fprop_desc_s &d) {
   return -1;
 }
 
-// Candidate configurations for shapes without a table entry, best first;
-// the first one that plans for the problem is used.
-const char *const kI8Candidates[] = {
-    // 3x3 (dilation 1): halo + register filter, then the all-LDS halo
-    "i8_halo_regfilter_mfma32x32x32_wg2x4_frag2x2_r3s3_ring4_hj2_pitch32_cps1",
-    "i8_halo_regfilter_mfma32x32x32_wg2x4_frag2x2_r3s3_ring3_hj6_pitch64_cps1",
-    "i8_halo_regfilter_mfma32x32x32_wg2x4_frag2x2_r3s3_ring4_hj2_pitch0_cps1",
-    "i8_halo_mfma32x32x32_wg2x4_frag2x2_r3s3_ring3",
-    "i8_halo_mfma32x32x32_wg1x4_frag2x2_r3s3_ring3",  // 64 output channels
-    // any shape: per-tap rings, (r, s)-outer when C/32 allows
-    "i8_mfma32x32x32_wg2x4_frag2x2_kt4_ring3_rsouter_true",
-    "i8_mfma32x32x32_wg2x4_frag2x2_kt2_ring6_rsouter_true",
-    "i8_mfma32x32x32_wg2x2_frag2x2_kt2_ring4_rsouter_false",
-    "i8_mfma32x32x32_wg1x4_frag2x1_kt4_ring4_rsouter_false",  // 64 ch x 128 px
-};
-const char *const kI8SmallCandidates[] = {
-    "i8_small_onepass_mfma32x32x32_frag1x1",
-    "i8_mfma32x32x32_wg1x2_frag1x1_kt4_ring4_rsouter_false",
-    "i8_mfma32x32x32_wg1x2_frag1x1_kt2_ring4_rsouter_true",
-    "i8_mfma32x32x32_wg1x1_frag1x1_kt2_ring4_rsouter_false",
-};
-
 // Configuration-selection model for shapes without a table entry, fitted to
 // shape-grid sweeps (fit_select.py): per configuration, its workgroups per
 // CU and the coefficients k[0..6] of its predicted time
@@ -395,27 +373,6 @@ conv_status_t conv2d_fprop_desc_create(conv2d_fprop_desc_t *out, int N, int C,
   const int cfg = lookup_shape(*d);
   if (cfg >= 0) ok = plan(*d, cfg);
   if (!ok) ok = plan_by_model(*d);
-  if (!ok && dtype == CONV_DTYPE_INT8) {
-    // Among the candidates that plan, the least estimated time: rounds of
-    // workgroups over the 256 CUs times the MFMA work of one tile (earlier
-    // candidates win ties).
-    const int64_t M = (int64_t)N * P * Q;
-    const bool small = M * K <= 128 * 128;
-    const char *const *cand = small ? kI8SmallCandidates : kI8Candidates;
-    const int nc = small ? (int)(sizeof(kI8SmallCandidates) / sizeof(kI8SmallCandidates[0]))
-                         : (int)(sizeof(kI8Candidates) / sizeof(kI8Candidates[0]));
-    int best = -1;
-    double best_cost = 0.0;
-    for (int i = 0; i < nc; ++i) {
-      const int c = find_config(dtype, cand[i]);
-      if (c < 0 || !plan(*d, c)) continue;
-      const I8Config &ic = *i8_config(c);
-      const double cost = (double)((d->grid + 255) / 256) * ic.bm * ic.bn;
-      if (best < 0 || cost < best_cost) best = c, best_cost = cost;
-    }
-    ok = best >= 0 && plan(*d, best);
-  }
-  if (!ok && dtype == CONV_DTYPE_FP32) ok = plan(*d, K <= 32 ? 1 : 0);
   if (!ok) {  // try every compiled configuration before giving up
     const int n = dtype == CONV_DTYPE_INT8 ? num_i8_configs() : kNumF32Configs;
     for (int c = 0; c < n && !ok; ++c) ok = plan(*d, c);

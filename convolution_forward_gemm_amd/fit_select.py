@@ -134,7 +134,7 @@ def summary_lines(title, ev):
         m = np.array([x[1] / x[2] for x in e])
         o = np.array([x[3] / x[2] for x in e])
         lines.append("  %-4s %3d shapes | model: mean %.3f median %.3f max %.2f, within 5%% of best %3.0f%%"
-                     " | previous rule: mean %.3f median %.3f max %.2f, within 5%% %3.0f%%"
+                     " | sweep-time default: mean %.3f median %.3f max %.2f, within 5%% %3.0f%%"
                      % (dt, len(e), m.mean(), np.median(m), m.max(), 100 * (m <= 1.05).mean(),
                         o.mean(), np.median(o), o.max(), 100 * (o <= 1.05).mean()))
     return lines
@@ -188,10 +188,12 @@ def main():
              % (len({tuple(r['shape']) for r in train}), len({tuple(r['shape']) for r in val})),
              "command: " + a.command,
              "(per shape: measured time of the configuration the model predicts fastest, over the",
-             " fastest measured; 'previous rule' is the least rounds-times-tile-area candidate)", ""]
+             " fastest measured; 'sweep-time default' is the configuration the library chose when",
+             " the sweep ran: for the kept data, the rule this model replaced, the least",
+             " rounds-times-tile-area candidate of a fixed list)", ""]
     lines += summary_lines("training shapes:", ev_t) + [""]
     lines += summary_lines("held-out shapes:", ev_v) + [""]
-    lines.append("held-out shapes, one by one (us: model's pick / fastest / previous rule):")
+    lines.append("held-out shapes, one by one (us: model's pick / fastest / sweep-time default):")
     for sh, mu, bu, du, pc, bc in ev_v:
         lines.append("  %-60s %9.2f %9.2f %9.2f  cfg %2d (fastest %2d)" % (sh, mu, bu, du, pc, bc))
     lines += ["", "per-configuration fit (shapes, occupancy, relative rms error):"]

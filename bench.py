@@ -43,6 +43,21 @@ def traffic_file(key: str) -> str:
     return os.path.join(PROFILES, "conv_i8_%s_traffic.json" % key)
 
 
+def committed_traffic(key: str, config: str):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summary of a workload, or None unless the kernel sources and
+    the configuration still match what was profiled."""
+    tf = traffic_file(key)
+    if not os.path.exists(tf):
+        return None
+    with open(tf) as f:
+        tr = json.load(f)
+    if (tr.get("kernel_source_hash") == kernel_source_hash() and tr.get("workload") == key
+            and tr.get("kernel_config") == config):
+        return tr.get("hbm_bytes_per_launch")
+    return None
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
@@ -400,16 +415,7 @@ def main():
     ops = conv_ops(wk, conv.P, conv.Q)
     tops = ops / (ms * 1e-3) / 1e12
 
-    # HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
-    # summary, only while the kernel sources still match what was profiled
-    traffic = None
-    tf = traffic_file(wk.key)
-    if os.path.exists(tf):
-        with open(tf) as f:
-            tr = json.load(f)
-        if (tr.get("kernel_source_hash") == kernel_source_hash() and tr.get("workload") == wk.key
-                and tr.get("kernel_config") == conv.config):
-            traffic = tr.get("hbm_bytes_per_launch")
+    traffic = committed_traffic(wk.key, conv.config)
 
     out = {
         "metric": METRIC,
@@ -461,7 +467,12 @@ def main():
         ms4 = time_device(torch, lambda: c4.run_ptr(x4.data_ptr(), w4d.data_ptr(), y4.data_ptr(), w4.alpha, s4), 2000, 3000)
         t4 = conv_ops(w4, c4.P, c4.Q) / (ms4 * 1e-3) / 1e12
         extra["c4_strided"] = {"ms": round(ms4, 6), "TOPS": round(t4, 3),
-                               "pct_of_int8_peak": round(100 * t4 / PEAK_INT8_TOPS, 2), "config": c4.config}
+                               "pct_of_int8_peak": round(100 * t4 / PEAK_INT8_TOPS, 2), "config": c4.config,
+                               "algorithmic_GBps": round(conv_bytes(w4, c4.P, c4.Q, 1) / (ms4 * 1e-3) / 1e9, 1)}
+        tr4 = committed_traffic("c4", c4.config)
+        if tr4 is not None:  # measured HBM bytes of one launch over this run's time
+            extra["c4_strided"]["hbm_traffic_bytes"] = tr4
+            extra["c4_strided"]["hbm_GBps"] = round(tr4 / (ms4 * 1e-3) / 1e9, 1)
         # per-output-channel scale and bias (conv2d_fprop_run_scaled) on the
         # headline workload
         gen = np.random.default_rng((2026, 31, 3))

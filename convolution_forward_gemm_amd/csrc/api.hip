@@ -74,7 +74,7 @@ int find_config(conv_dtype_t dtype, const char *name) {
 }
 
 // Per-shape table: the configuration chosen for a problem by sweep, by
-// name.  Shapes not listed fall back to the heuristic below.
+// name.  Other shapes are planned by the selection model below.
 struct ShapeEntry {
   conv_dtype_t dtype;
   int N, C, H, W, K, R, S, ph, pw, sh, sw, dh, dw;

@@ -78,7 +78,9 @@ typedef enum {
  * run calls on different streams. */
 typedef struct conv2d_fprop_desc_s *conv2d_fprop_desc_t;
 
-/* Validate a problem and choose its kernel configuration.
+/* Validate a problem and choose its kernel configuration: the tuned
+ * configuration of a per-shape table, else the one a cost model fitted to
+ * configuration sweeps predicts fastest among those that can run it.
  *   out         receives the descriptor (set to NULL on error)
  *   N,C,H,W     input batch, channels, height, width        (> 0)
  *   K,R,S       output channels, filter height, filter width (> 0)
@@ -100,8 +102,9 @@ conv_status_t conv2d_fprop_desc_destroy(conv2d_fprop_desc_t desc);
 conv_status_t conv2d_fprop_desc_get_output_dims(conv2d_fprop_desc_t desc,
                                                 int *P, int *Q);
 
-/* NUL-terminated text naming the chosen kernel configuration (tile shape,
- * stages, launch grid), truncated to buf_size bytes. */
+/* NUL-terminated text naming the chosen kernel configuration, truncated to
+ * buf_size bytes: "config=<index> <name> tile=<ch>ch x <px>px grid=<work-
+ * groups> lds=<bytes per workgroup> threads=<per workgroup>". */
 conv_status_t conv2d_fprop_desc_get_config(conv2d_fprop_desc_t desc, char *buf,
                                            size_t buf_size);
 

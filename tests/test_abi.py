@@ -212,7 +212,7 @@ def test_binding_has_no_cpu_fallback():
 
 def test_shape_table_choices(b):
     # the per-shape table names configurations; a name that no longer exists
-    # would silently fall back to the heuristic
+    # would silently fall back to the selection model
     from convolution_forward_gemm_amd import workloads as wl
     expect = {
         "c1": "i8_small_onepass_mfma32x32x32_frag1x1",

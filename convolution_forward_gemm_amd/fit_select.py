@@ -183,9 +183,12 @@ def main():
         models[key] = (occ, coef)
         fits.append((key, len(rows), occ, res))
     write_table(models, a.table)
-    ev_t, ev_v = evaluate(models, train), evaluate(models, val)
+    # a validation shape that is also in the training grid is not held out
+    seen = {tuple(r["shape"]) for r in train}
+    held = [r for r in val if tuple(r["shape"]) not in seen]
+    ev_t, ev_v = evaluate(models, train), evaluate(models, held)
     lines = ["Configuration-selection model: fit on %d shapes, checked on %d held-out shapes"
-             % (len({tuple(r['shape']) for r in train}), len({tuple(r['shape']) for r in val})),
+             % (len(seen), len({tuple(r['shape']) for r in held})),
              "command: " + a.command,
              "(per shape: measured time of the configuration the model predicts fastest, over the",
              " fastest measured; 'sweep-time default' is the configuration the library chose when",

@@ -48,3 +48,34 @@ def test_summarize_trace_maps_kernels_in_sweep_order(tmp_path):
     assert got == {i: dur[i] / 1e3 for i in idx}
     chosen = [r for r in rows if r.endswith("<- chosen")]
     assert len(chosen) == 1 and int(chosen[0].split()[0]) == default
+
+
+def test_shape_grids_are_fixed_and_disjoint():
+    # the kept sweep data are keyed by these shapes: the grids must not drift,
+    # and no held-out shape may appear in the training grid
+    train, val = sweep.grid_shapes("train"), sweep.grid_shapes("validate")
+    assert train == sweep.grid_shapes("train") and val == sweep.grid_shapes("validate")
+    assert len(train) == 554 and len(val) == 43
+    # the only shared shape: 3x3 C256 at N = 4, also one GPU's share of the
+    # batch-sharded N = 32 workload (the fit summary leaves it out of the
+    # held-out figures)
+    assert set(train) & set(val) == {("int8", 4, 256, 28, 28, 256, 3, 3, 1, 1, 1, 1, 1, 1)}
+    for sh in train + val:
+        dt, N, C, H, W, K, R, S, ph, pw, sth, stw, dh, dw = sh
+        conv = b.Conv2dFprop(N, C, H, W, K, R, S, pad=(ph, pw), stride=(sth, stw), dil=(dh, dw),
+                             dtype=dt)
+        assert conv.P >= 1 and conv.Q >= 1
+
+
+def test_kept_sweeps_cover_the_grids():
+    import os
+    from convolution_forward_gemm_amd import fit_select as fs
+    tuning = os.path.join(os.path.dirname(sweep.__file__), "tuning")
+    for kind in ("train", "validate"):
+        rows = fs.load(os.path.join(tuning, "select_%s.csv.gz" % kind))
+        assert {tuple(r["shape"]) for r in rows} == set(sweep.grid_shapes(kind))
+        # exactly one library default per shape
+        per = {}
+        for r in rows:
+            per[tuple(r["shape"])] = per.get(tuple(r["shape"]), 0) + int(r["default"])
+        assert set(per.values()) == {1}

@@ -247,7 +247,7 @@ def _conv_kernel(names):
     return max(conv, key=lambda n: names[n])
 
 
-def summarize_trace(key, trace_dir, command):
+def summarize_trace(key, trace_dir, command, tag=""):
     from convolution_forward_gemm_amd import workloads as wl
     rows = _csv_rows(_find(trace_dir, "kernel_stats.csv"))
     calls = {r["Name"]: int(r["Calls"]) for r in rows}
@@ -270,7 +270,7 @@ def summarize_trace(key, trace_dir, command):
     ops = conv_ops(wk, conv.P, conv.Q)
     lines += ["", "conv kernel average %.2f us -> %.1f TOPS = %.1f%% of the %.1f POP/s int8 MFMA peak"
               % (avg / 1e3, ops / avg / 1e3, 100 * ops / avg / 1e3 / PEAK_INT8_TOPS, PEAK_INT8_TOPS / 1e3)]
-    out = os.path.join(PROFILES, "conv_i8_%s_kernel_trace.txt" % key)
+    out = os.path.join(PROFILES, "conv_i8_%s%s_kernel_trace.txt" % (key, tag))
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     return out
@@ -326,7 +326,7 @@ def summarize_traffic(key, fetch_dir, write_dir, copy_mib, commands):
     return out
 
 
-def summarize_counters(key, dirs, commands):
+def summarize_counters(key, dirs, commands, tag=""):
     """Average per-dispatch value of every counter collected for the conv
     kernel, over rocprofv3 --pmc runs of this script."""
     from convolution_forward_gemm_amd import workloads as wl
@@ -351,10 +351,14 @@ def summarize_counters(key, dirs, commands):
     lines += ["", "| counter | per dispatch | dispatches |", "|---|---|---|"]
     for c in sorted(acc):
         lines.append("| %s | %.1f | %d |" % (c, acc[c] / cnt[c], cnt[c]))
-    out = os.path.join(PROFILES, "conv_i8_%s_counters.md" % key)
+    out = os.path.join(PROFILES, "conv_i8_%s%s_counters.md" % (key, tag))
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     return out
+
+
+def _tag(args):
+    return "" if args.config is None else "_cfg%d" % args.config
 
 
 def main():
@@ -382,13 +386,17 @@ def main():
                          "output directories of this script, then exit")
     ap.add_argument("--command", action="append", default=[],
                     help="with --summarize-*: the profiling command(s) to record")
+    ap.add_argument("--config", type=int, default=None,
+                    help="run another compiled configuration of the workload (for profiling "
+                         "alternatives; summaries then carry a _cfg<N> suffix)")
     args = ap.parse_args()
     if args.summarize_counters:
-        print(summarize_counters(args.workload, args.summarize_counters, args.command))
+        print(summarize_counters(args.workload, args.summarize_counters, args.command, _tag(args)))
         return
     if args.summarize_trace or args.summarize_traffic:
         if args.summarize_trace:
-            print(summarize_trace(args.workload, args.summarize_trace, " && ".join(args.command)))
+            print(summarize_trace(args.workload, args.summarize_trace, " && ".join(args.command),
+                                  _tag(args)))
         if args.summarize_traffic:
             print(summarize_traffic(args.workload, *args.summarize_traffic,
                                     args.calib_copy_mib or 256, args.command))
@@ -404,6 +412,8 @@ def main():
 
     wk = wl.WORKLOADS[args.workload]
     conv, xd, wd, yd, host_inputs = setup(wk, torch, b)
+    if args.config is not None:  # profiling another configuration; not the reported choice
+        conv.set_config(args.config)
     stream = torch.cuda.current_stream().cuda_stream
     xp, wp, yp = xd.data_ptr(), wd.data_ptr(), yd.data_ptr()
 

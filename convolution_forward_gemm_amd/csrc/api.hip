@@ -84,12 +84,13 @@ struct ShapeEntry {
 const ShapeEntry kShapeTable[] = {
     // int8 3x3 N1 C32 8x8 K32 and 1x1 N2 C128 8x8 K128: launch-latency
     // bound, chosen by back-to-back time per call (graph replay); one wave
-    // per 32x32 tile fetches its whole reduction in one memory round trip
-    // (one-pass kernel, rolled loops, small code)
+    // per 32x32 tile loads its whole reduction straight into registers in
+    // one memory round trip, each MFMA waiting only for its own tap
+    // (unrolled for the filter size and channel count)
     {CONV_DTYPE_INT8, 1, 32, 8, 8, 32, 3, 3, 1, 1, 1, 1, 1, 1,
-     "i8_small_onepass_mfma32x32x32_frag1x1"},
+     "i8_tiny_unrolled_r3s3_cb1_mfma32x32x32_frag1x1"},
     {CONV_DTYPE_INT8, 2, 128, 8, 8, 128, 1, 1, 0, 0, 1, 1, 1, 1,
-     "i8_small_onepass_mfma32x32x32_frag1x1"},
+     "i8_tiny_unrolled_r1s1_cb4_mfma32x32x32_frag1x1"},
     // int8 3x3 N32 C256 28x28 K256: activation halo in LDS (row pitch 32),
     // filter fragments in registers, 128 ch x 256 px tiles, 8 waves of 64x64
     {CONV_DTYPE_INT8, 32, 256, 28, 28, 256, 3, 3, 1, 1, 1, 1, 1, 1,
@@ -219,6 +220,10 @@ bool plan(conv2d_fprop_desc_s &d, int cfg) {
     p.HV = p.WV = p.halo_dpp = p.halo_bytes = p.stage_bytes = 0;
     p.lds_bytes = c.lds_bytes;
     if ((c.kind == 1 || c.kind == 2) && !plan_halo(d, c, M, p)) return false;
+    if (c.kind == 4) {  // unrolled for one filter size and channel count; no LDS
+      if (d.R != c.fr || d.S != c.fs || d.C / 32 != c.kt) return false;
+      p.lds_bytes = 0;
+    }
     if (c.kind == 3) {  // the whole reduction in LDS: ntaps filter + pixel fragments
       // every fragment's DMA is in flight at once: at most 63 (vmcnt range)
       const int64_t loads = (int64_t)p.ntaps * (1 + c.bn / 32);

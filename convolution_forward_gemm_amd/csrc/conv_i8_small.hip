@@ -124,6 +124,90 @@ static hipError_t launch_i8_small(const int8_t *x, const int8_t *w, int8_t *y, c
                    : launch_i8_small_pc<FP, false>(x, w, y, p, grid, s);
 }
 
+// Fully unrolled one-pass variant for one filter size and channel count
+// (R x S taps over CB channel blocks, fixed at compile time), one 32 x 32
+// tile per wave.  Every tap's filter and pixel fragments are loaded straight
+// into registers, in tap order; each MFMA then waits only for its own tap's
+// two loads (the compiler's in-order vmcnt accounting), so the matrix work
+// starts when the first tap lands rather than after the last, and no LDS
+// round trip sits between the loads and the MFMAs.  Even and odd taps
+// accumulate separately (two independent MFMA chains) and are summed at
+// the end; integer sums, so the result is the same.
+template <int R, int S, int CB, bool PC>
+__global__ void __launch_bounds__(64)
+conv_i8_tiny_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ w,
+                    int8_t *__restrict__ y, I8Params p) {
+  constexpr int NT = R * S * CB;
+  const int lane = threadIdx.x;
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+  const int ktile = blockIdx.x % p.KBLK;
+  const int mtile = blockIdx.x / p.KBLK;
+  const int m0 = mtile * 32;
+
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, p.x_bytes);
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(w, p.w_bytes);
+  const uint32_t a_off = (uint32_t)((ktile * 32 + l32) * 32 + 16 * half);
+  int h0 = -(1 << 28), w0 = 0;
+  uint32_t pbase = 0;
+  const int m = m0 + l32;
+  if (m < p.M) {
+    const int n = m / p.PQ;
+    const int pq = m - n * p.PQ;
+    const int op = pq / p.Q;
+    const int oq = pq - op * p.Q;
+    h0 = op * p.sh - p.ph;
+    w0 = oq * p.sw - p.pw;
+    pbase = (uint32_t)(n * CB * p.HW * 32 + 16 * half);
+  }
+  const int KB32 = p.K * 32;
+  v4i a[NT], b[NT];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        const int g = (cb * R + r) * S + s;
+        a[g] = load_b128_s(wr, a_off, g * KB32);
+        const int h = h0 + r * p.dh;
+        const int ww = w0 + s * p.dw;
+        const bool in = (unsigned)h < (unsigned)p.H && (unsigned)ww < (unsigned)p.W;
+        b[g] = load_b128(xr, in ? pbase + (uint32_t)(((cb * p.H + h) * p.W + ww) * 32) : OOB_OFFSET);
+      }
+  // every load goes out before the first MFMA (the scheduler would otherwise
+  // trade registers for loads issued behind earlier waits: several memory
+  // round trips instead of one)
+  __builtin_amdgcn_sched_barrier(0);
+  v16i acc[2] = {v16i{0}, v16i{0}};
+#pragma unroll
+  for (int g = 0; g < NT; ++g)
+    acc[g & 1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[g], b[g], acc[g & 1], 0, 0, 0);
+  v16i sum[1][1] = {{acc[0] + acc[1]}};
+  store_i8_tile<PC, 1, 1>(sum, y, p, m0, ktile, lane);
+}
+
+template <int R, int S, int CB, bool PC>
+static hipError_t launch_i8_tiny_pc(const int8_t *x, const int8_t *w, int8_t *y, const I8Params &p,
+                                    int grid, hipStream_t s) {
+  hipLaunchKernelGGL((conv_i8_tiny_kernel<R, S, CB, PC>), dim3(grid), dim3(64), 0, s, x, w, y, p);
+  return hipGetLastError();
+}
+
+template <int R, int S, int CB>
+static hipError_t launch_i8_tiny(const int8_t *x, const int8_t *w, int8_t *y, const I8Params &p,
+                                 int grid, hipStream_t s) {
+  return p.alpha_k ? launch_i8_tiny_pc<R, S, CB, true>(x, w, y, p, grid, s)
+                   : launch_i8_tiny_pc<R, S, CB, false>(x, w, y, p, grid, s);
+}
+
+// kind 4: fr x fs filter and kt channel blocks exactly
+#define I8_TINY_CFG(R, S, CB)                                                       \
+  I8Config {                                                                        \
+    "i8_tiny_unrolled_r" #R "s" #S "_cb" #CB "_mfma32x32x32_frag1x1", 32, 32, 64, 0, CB, 0, \
+        &launch_i8_tiny<R, S, CB>, 4, R, S, 1, 1, 0, 0, 1                           \
+  }
+
 #define I8_SMALL_CFG(FP)                                                            \
   I8Config {                                                                        \
     "i8_small_onepass_mfma32x32x32_frag1x" #FP, 32, 32 * FP, 64, 0, 0, 0,           \
@@ -133,6 +217,8 @@ static hipError_t launch_i8_small(const int8_t *x, const int8_t *w, int8_t *y, c
 I8Config kI8SmallConfigs[] = {
     I8_SMALL_CFG(1),  // 32 ch x 32 px per wave
     I8_SMALL_CFG(2),  // 32 ch x 64 px per wave
+    I8_TINY_CFG(3, 3, 1),  // 3x3 over 32 channels
+    I8_TINY_CFG(1, 1, 4),  // 1x1 over 128 channels
 };
 int kNumI8SmallConfigs = sizeof(kI8SmallConfigs) / sizeof(kI8SmallConfigs[0]);
 

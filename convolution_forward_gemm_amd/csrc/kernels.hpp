@@ -43,14 +43,16 @@ struct I8Config {
   int bn;       // output pixels per workgroup
   int threads;
   int lds_bytes;
-  int kt;        // taps per stage
+  int kt;        // taps per stage (kind 4: channel blocks)
   int rs_outer;  // 1: needs (C/32) % kt == 0
   I8LaunchFn launch;
   // Halo kernels (kind 1, 2): compiled filter size, waves, stages, and the
   // most halo DMA blocks per wave per stage they can issue.
   int kind;      // 0: per-tap fragment ring, 1: LDS activation halo + LDS
                  // filter taps, 2: LDS activation halo + filter in registers,
-                 // 3: one-pass kernel for small problems (whole reduction in LDS)
+                 // 3: one-pass kernel for small problems (whole reduction in LDS),
+                 // 4: the same unrolled for one filter size and channel count
+                 // (fr x fs taps over kt channel blocks), in registers
   int fr, fs, nwaves, ns, hj;
   int pw;   // kind 2: halo row pitch in LDS (0: the halo width; > 0: fixed, dilation 1)
   int cps;  // kind 2: channel blocks per ring stage (C/32 must be a multiple)

@@ -91,13 +91,22 @@ def features(r, occ):
     return np.array([1.0, R, R * Wt, R * L, R * C / 100, R * Rf * Sf / 10, r["grid"] * Wt / 1e3])
 
 
+# With fewer shapes than coefficients a configuration gets the three-term
+# model t = a + b * R + g * G * W (the other coefficients zero).
+FULL_ROWS = 8
+REDUCED = (0, 1, 6)
+
+
 def fit_config(rows):
     """(occ, coefficients, relative rms) minimising the relative error."""
     t = np.array([r["us"] for r in rows])
+    cols = list(range(7)) if len(rows) >= FULL_ROWS else list(REDUCED)
     best = None
     for occ in OCC_CHOICES:
         A = np.stack([features(r, occ) for r in rows]) / t[:, None]
-        coef, _ = nnls(A, np.ones(len(rows)))
+        sub, _ = nnls(A[:, cols], np.ones(len(rows)))
+        coef = np.zeros(A.shape[1])
+        coef[cols] = sub
         res = float(np.sqrt(np.mean((A @ coef - 1.0) ** 2)))
         if best is None or res < best[2] - 1e-9:
             best = (occ, coef, res)
@@ -177,7 +186,7 @@ def main():
         per[(r["shape"][0], r["name"])].append(r)
     models, fits = {}, []
     for key, rows in sorted(per.items()):
-        if len(rows) < 8:  # too few shapes to fit seven coefficients
+        if len(rows) < len(REDUCED):  # too few shapes even for the reduced model
             continue
         occ, coef, res = fit_config(rows)
         models[key] = (occ, coef)

@@ -314,9 +314,10 @@ def _median_us(torch, fn, target_us=300.0, reps=3):
     return ts[len(ts) // 2]
 
 
-def run_shape_grid(kind, out_path):
-    """Time every configuration that runs each shape of the grid; one JSON
-    line per (shape, configuration) appended to out_path."""
+def run_shape_grid(kind, out_path, only=None):
+    """Time every configuration that runs each shape of the grid (or only the
+    named ones); one JSON line per (shape, configuration) appended to
+    out_path."""
     import torch
     from . import binding as b
 
@@ -358,6 +359,8 @@ def run_shape_grid(kind, out_path):
                     if e.status != b.CONV_ERR_UNSUPPORTED:
                         raise
                     continue
+                if only and _parse_config(conv.config)["name"] not in only:
+                    continue
                 us = _median_us(torch, lambda: conv.run_ptr(xp, wp, yp, alpha, s))
                 rec = {"kind": kind, "shape": list(sh)}
                 rec.update(_parse_config(conv.config))
@@ -383,9 +386,10 @@ def main():
     ap.add_argument("--out-dir", default=os.path.join(ROOT, "profiles"))
     ap.add_argument("--grid", choices=["train", "validate"], help="time a shape grid (model fit)")
     ap.add_argument("--out", help="with --grid: JSON-lines output file")
+    ap.add_argument("--only", help="with --grid: comma-separated configuration names to time")
     a = ap.parse_args()
     if a.grid:
-        run_shape_grid(a.grid, a.out)
+        run_shape_grid(a.grid, a.out, set(a.only.split(",")) if a.only else None)
         return
     if a.summarize_trace:
         print(summarize_trace(a.workload, a.summarize_trace, a.command, a.out_dir, a.sweep_log))

@@ -115,7 +115,8 @@ def test_set_config(b):
     shapes = [b.Conv2dFprop(*GOOD[:7], pad=1),
               b.Conv2dFprop(32, 128, 56, 56, 256, 3, 3, pad=1, stride=2),
               b.Conv2dFprop(2, 256, 9, 7, 320, 3, 3, pad=1),
-              b.Conv2dFprop(1, 32, 8, 8, 32, 3, 3, pad=1)]
+              b.Conv2dFprop(1, 32, 8, 8, 32, 3, 3, pad=1),
+              b.Conv2dFprop(2, 128, 8, 8, 128, 1, 1)]
     names = set()
     for i in range(b.num_configs("int8")):
         ok = 0
@@ -215,8 +216,8 @@ def test_shape_table_choices(b):
     # would silently fall back to the selection model
     from convolution_forward_gemm_amd import workloads as wl
     expect = {
-        "c1": "i8_small_onepass_mfma32x32x32_frag1x1",
-        "c2": "i8_small_onepass_mfma32x32x32_frag1x1",
+        "c1": "i8_tiny_unrolled_r3s3_cb1_mfma32x32x32_frag1x1",
+        "c2": "i8_tiny_unrolled_r1s1_cb4_mfma32x32x32_frag1x1",
         "c3": "i8_halo_regfilter_mfma32x32x32_wg2x4_frag2x2_r3s3_ring4_hj2_pitch32_cps1",
         "c4": "i8_halo_regfilter_mfma32x32x32_wg2x4_frag2x2_r3s3_ring3_hj6_pitch64_cps1",
         "c5": "f32_mfma32x32x2_16waves_frag2x2_cc4_depth3_dbuf",

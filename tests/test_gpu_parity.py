@@ -146,6 +146,8 @@ RAGGED = [
     (3, 256, 5, 6, 96, 1, 1, (0, 0), (1, 1), (1, 1)),      # 1x1, C/32 = 8
     (3, 64, 23, 21, 96, 3, 3, (1, 1), (2, 2), (1, 1)),     # stride 2, ragged M and K tiles
     (1, 64, 56, 56, 64, 3, 3, (1, 1), (2, 2), (1, 1)),     # stride 2, 57-column halo rows
+    (3, 128, 5, 7, 96, 1, 1, (0, 0), (1, 1), (1, 1)),      # 1x1 over 128 channels, ragged M
+    (2, 32, 11, 9, 64, 3, 3, (2, 1), (2, 1), (1, 2)),      # 3x3 over 32 channels, stride, dilation
 ]
 
 

@@ -224,6 +224,10 @@ bool plan(conv2d_fprop_desc_s &d, int cfg) {
       if (d.R != c.fr || d.S != c.fs || d.C / 32 != c.kt) return false;
       p.lds_bytes = 0;
     }
+    if (c.kind == 5) {  // unrolled for exactly kt reduction taps; no LDS
+      if (p.ntaps != c.kt) return false;
+      p.lds_bytes = 0;
+    }
     if (c.kind == 3) {  // the whole reduction in LDS: ntaps filter + pixel fragments
       // every fragment's DMA is in flight at once: at most 63 (vmcnt range)
       const int64_t loads = (int64_t)p.ntaps * (1 + c.bn / 32);

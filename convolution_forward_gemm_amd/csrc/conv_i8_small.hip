@@ -201,6 +201,83 @@ static hipError_t launch_i8_tiny(const int8_t *x, const int8_t *w, int8_t *y, co
                    : launch_i8_tiny_pc<R, S, CB, false>(x, w, y, p, grid, s);
 }
 
+// The same for any problem with exactly NT reduction taps (channel blocks x
+// filter taps): the (cb, r, s) walk runs at run time, the load and MFMA
+// sequence is unrolled for NT.
+template <int NT, bool PC>
+__global__ void __launch_bounds__(64)
+conv_i8_tinyn_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ w,
+                     int8_t *__restrict__ y, I8Params p) {
+  const int lane = threadIdx.x;
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+  const int ktile = blockIdx.x % p.KBLK;
+  const int mtile = blockIdx.x / p.KBLK;
+  const int m0 = mtile * 32;
+
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, p.x_bytes);
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(w, p.w_bytes);
+  const uint32_t a_off = (uint32_t)((ktile * 32 + l32) * 32 + 16 * half);
+  int h0 = -(1 << 28), w0 = 0;
+  uint32_t pbase = 0;
+  const int m = m0 + l32;
+  if (m < p.M) {
+    const int n = m / p.PQ;
+    const int pq = m - n * p.PQ;
+    const int op = pq / p.Q;
+    const int oq = pq - op * p.Q;
+    h0 = op * p.sh - p.ph;
+    w0 = oq * p.sw - p.pw;
+    pbase = (uint32_t)(n * p.CB * p.HW * 32 + 16 * half);
+  }
+  const int KB32 = p.K * 32;
+  v4i a[NT], b[NT];
+  int cb = 0, r = 0, s = 0;
+#pragma unroll
+  for (int g = 0; g < NT; ++g) {
+    a[g] = load_b128_s(wr, a_off, g * KB32);
+    const int h = h0 + r * p.dh;
+    const int ww = w0 + s * p.dw;
+    const bool in = (unsigned)h < (unsigned)p.H && (unsigned)ww < (unsigned)p.W;
+    b[g] = load_b128(xr, in ? pbase + (uint32_t)(((cb * p.H + h) * p.W + ww) * 32) : OOB_OFFSET);
+    if (++s == p.S) {
+      s = 0;
+      if (++r == p.R) {
+        r = 0;
+        ++cb;
+      }
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);  // every load before the first MFMA
+  v16i acc[2] = {v16i{0}, v16i{0}};
+#pragma unroll
+  for (int g = 0; g < NT; ++g)
+    acc[g & 1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[g], b[g], acc[g & 1], 0, 0, 0);
+  v16i sum[1][1] = {{acc[0] + acc[1]}};
+  store_i8_tile<PC, 1, 1>(sum, y, p, m0, ktile, lane);
+}
+
+template <int NT, bool PC>
+static hipError_t launch_i8_tinyn_pc(const int8_t *x, const int8_t *w, int8_t *y, const I8Params &p,
+                                     int grid, hipStream_t s) {
+  hipLaunchKernelGGL((conv_i8_tinyn_kernel<NT, PC>), dim3(grid), dim3(64), 0, s, x, w, y, p);
+  return hipGetLastError();
+}
+
+template <int NT>
+static hipError_t launch_i8_tinyn(const int8_t *x, const int8_t *w, int8_t *y, const I8Params &p,
+                                  int grid, hipStream_t s) {
+  return p.alpha_k ? launch_i8_tinyn_pc<NT, true>(x, w, y, p, grid, s)
+                   : launch_i8_tinyn_pc<NT, false>(x, w, y, p, grid, s);
+}
+
+// kind 5: exactly kt reduction taps (C/32 * R * S)
+#define I8_TINYN_CFG(NT)                                                            \
+  I8Config {                                                                        \
+    "i8_tiny_unrolled_taps" #NT "_mfma32x32x32_frag1x1", 32, 32, 64, 0, NT, 0,      \
+        &launch_i8_tinyn<NT>, 5, 0, 0, 1, 1, 0, 0, 1                                \
+  }
+
 // kind 4: fr x fs filter and kt channel blocks exactly
 #define I8_TINY_CFG(R, S, CB)                                                       \
   I8Config {                                                                        \
@@ -219,6 +296,10 @@ I8Config kI8SmallConfigs[] = {
     I8_SMALL_CFG(2),  // 32 ch x 64 px per wave
     I8_TINY_CFG(3, 3, 1),  // 3x3 over 32 channels
     I8_TINY_CFG(1, 1, 4),  // 1x1 over 128 channels
+    // any filter, exactly NT = C/32 * R * S reduction taps
+    I8_TINYN_CFG(2), I8_TINYN_CFG(3), I8_TINYN_CFG(4), I8_TINYN_CFG(6), I8_TINYN_CFG(8),
+    I8_TINYN_CFG(9), I8_TINYN_CFG(12), I8_TINYN_CFG(16), I8_TINYN_CFG(18), I8_TINYN_CFG(25),
+    I8_TINYN_CFG(27), I8_TINYN_CFG(36),
 };
 int kNumI8SmallConfigs = sizeof(kI8SmallConfigs) / sizeof(kI8SmallConfigs[0]);
 

@@ -43,7 +43,7 @@ struct I8Config {
   int bn;       // output pixels per workgroup
   int threads;
   int lds_bytes;
-  int kt;        // taps per stage (kind 4: channel blocks)
+  int kt;        // taps per stage (kind 4: channel blocks; kind 5: reduction taps)
   int rs_outer;  // 1: needs (C/32) % kt == 0
   I8LaunchFn launch;
   // Halo kernels (kind 1, 2): compiled filter size, waves, stages, and the
@@ -52,7 +52,8 @@ struct I8Config {
                  // filter taps, 2: LDS activation halo + filter in registers,
                  // 3: one-pass kernel for small problems (whole reduction in LDS),
                  // 4: the same unrolled for one filter size and channel count
-                 // (fr x fs taps over kt channel blocks), in registers
+                 // (fr x fs taps over kt channel blocks), in registers,
+                 // 5: the same for any problem of exactly kt reduction taps
   int fr, fs, nwaves, ns, hj;
   int pw;   // kind 2: halo row pitch in LDS (0: the halo width; > 0: fixed, dilation 1)
   int cps;  // kind 2: channel blocks per ring stage (C/32 must be a multiple)

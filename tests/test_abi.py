@@ -117,6 +117,10 @@ def test_set_config(b):
               b.Conv2dFprop(2, 256, 9, 7, 320, 3, 3, pad=1),
               b.Conv2dFprop(1, 32, 8, 8, 32, 3, 3, pad=1),
               b.Conv2dFprop(2, 128, 8, 8, 128, 1, 1)]
+    # one shape per tap count of the tap-count-unrolled kernels (C/32 * R * S)
+    for C, R, S in ((64, 1, 1), (96, 1, 1), (64, 1, 3), (256, 1, 1), (128, 1, 3), (512, 1, 1),
+                    (64, 3, 3), (32, 5, 5), (96, 3, 3)):
+        shapes.append(b.Conv2dFprop(1, C, 7, 7, 32, R, S))
     names = set()
     for i in range(b.num_configs("int8")):
         ok = 0

@@ -148,6 +148,13 @@ RAGGED = [
     (1, 64, 56, 56, 64, 3, 3, (1, 1), (2, 2), (1, 1)),     # stride 2, 57-column halo rows
     (3, 128, 5, 7, 96, 1, 1, (0, 0), (1, 1), (1, 1)),      # 1x1 over 128 channels, ragged M
     (2, 32, 11, 9, 64, 3, 3, (2, 1), (2, 1), (1, 2)),      # 3x3 over 32 channels, stride, dilation
+    (1, 64, 9, 10, 96, 3, 3, (1, 0), (1, 2), (2, 1)),      # 18 taps
+    (2, 32, 7, 8, 32, 5, 5, (2, 2), (1, 1), (1, 1)),       # 25 taps, padding wider than half
+    (2, 64, 6, 5, 64, 1, 1, (0, 0), (1, 1), (1, 1)),       # 2 taps
+    (1, 32, 8, 9, 32, 2, 3, (1, 1), (1, 1), (1, 1)),       # 6 taps, even filter height
+    (1, 128, 6, 6, 64, 1, 3, (0, 1), (1, 1), (1, 1)),      # 12 taps
+    (2, 512, 3, 4, 32, 1, 1, (0, 0), (1, 1), (1, 1)),      # 16 taps
+    (1, 96, 5, 5, 32, 3, 3, (1, 1), (2, 2), (1, 1)),       # 27 taps, stride 2
 ]
 
 

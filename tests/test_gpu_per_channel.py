@@ -52,6 +52,8 @@ CASES = [
     (2, 256, 9, 7, 320, 3, 3, (1, 1), (1, 1), (1, 1)),     # ragged K tile
     (3, 64, 23, 21, 96, 3, 3, (1, 1), (2, 2), (1, 1)),     # stride 2
     (3, 96, 7, 7, 32, 1, 1, (0, 0), (1, 1), (1, 1)),       # 1x1
+    (2, 32, 8, 8, 64, 3, 3, (1, 1), (1, 1), (1, 1)),       # 3x3 over 32 channels (unrolled tiny)
+    (2, 128, 6, 5, 64, 1, 1, (0, 0), (1, 1), (1, 1)),      # 1x1 over 128 channels (unrolled tiny)
 ]
 
 

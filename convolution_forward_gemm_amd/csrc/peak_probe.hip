@@ -81,6 +81,28 @@ __global__ void __launch_bounds__(256) mfma_i8_rand(const v4i *__restrict__ src,
   out[blockIdx.x * 256 + t] = s;
 }
 
+// The same random operands on the 16 x 16 x 64 int8 MFMA (half the work
+// per instruction, twice the instructions for the same operations).
+__global__ void __launch_bounds__(256) mfma_i8_rand16(const v4i *__restrict__ src, v16i *out, int iters) {
+  int t = threadIdx.x;
+  v4i a[4], b[4];
+  for (int k = 0; k < 4; ++k) {
+    a[k] = src[(k * 256 + t) & 2047];
+    b[k] = src[((k + 4) * 256 + t) & 2047];
+  }
+  v4i c[16] = {};
+  for (int i = 0; i < iters; i += 4) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        c[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[(j + u) & 3], b[((j >> 2) + u) & 3], c[j], 0, 0, 0);
+  }
+  v4i s = {};
+  for (int k = 0; k < 16; ++k) s += c[k];
+  out[blockIdx.x * 256 + t] = v16i{s[0], s[1], s[2], s[3]};
+}
+
 // The same with K independent v_add_u32 issued by the wave after every
 // MFMA: how much vector ALU work one wave can hide behind its own MFMAs.
 template <int K>
@@ -284,6 +306,14 @@ int main() {
       const double tops = 4 * 2.0 * 32 * 32 * 32 * 8 * (double)rit * g * 4 / ms / 1e9;
       printf("int8 MFMA, random operands, %3d CUs : %8.1f TOPS (%.1f per-CU rate x %d CUs)\n", g, tops,
              tops / g * ncu, ncu);
+      CHECK(hipEventRecord(e0));
+      for (int r = 0; r < 4; ++r)
+        hipLaunchKernelGGL(mfma_i8_rand16, dim3(g), dim3(256), 0, 0, (const v4i *)rnd, (v16i *)out, rit);
+      CHECK(hipEventRecord(e1));
+      CHECK(hipEventSynchronize(e1));
+      CHECK(hipEventElapsedTime(&ms, e0, e1));
+      printf("int8 MFMA 16x16x64, random operands, %3d CUs : %8.1f TOPS\n", g,
+             4 * 2.0 * 16 * 16 * 64 * 16 * (double)rit * g * 4 / ms / 1e9);
     }
     CHECK(hipFree(rnd));
   }

@@ -745,6 +745,13 @@ I8Config kI8HaloConfigs[] = {
     // filter in the LDS ring as well, fetched once per workgroup
     I8_HALO_LF_CFG(2, 4, 2, 2, 3, 3, 3, 2, 32, 1),   // 8 waves of 64x64
     I8_HALO_LF_CFG(2, 2, 2, 4, 3, 3, 3, 4, 32, 1),   // 4 waves of 64x128
+    // small tiles for problems that give too few large ones (64 x 64,
+    // 64 x 128, 128 x 64: four waves of one or two 32 x 32 fragments)
+    I8_HALO_AD_CFG(2, 2, 1, 1, 3, 3, 4, 2, 32, 1),
+    I8_HALO_AD_CFG(2, 2, 1, 2, 3, 3, 4, 2, 32, 1),
+    I8_HALO_AD_CFG(2, 2, 2, 1, 3, 3, 4, 2, 32, 1),
+    I8_HALO_AD_CFG(2, 2, 1, 1, 3, 3, 3, 4, 64, 1),
+    I8_HALO_AD_CFG(2, 2, 1, 2, 3, 3, 3, 6, 64, 1),
 };
 int kNumI8HaloConfigs = sizeof(kI8HaloConfigs) / sizeof(kI8HaloConfigs[0]);
 

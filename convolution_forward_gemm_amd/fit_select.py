@@ -120,7 +120,7 @@ def predict(model, r):
 
 def evaluate(models, rows):
     """Per shape: (shape, measured us of the predicted choice, best us,
-    default us, predicted config, best config)."""
+    default us, predicted configuration name, fastest configuration name)."""
     by = collections.defaultdict(list)
     for r in rows:
         by[tuple(r["shape"])].append(r)
@@ -130,7 +130,7 @@ def evaluate(models, rows):
         pick = min(cand, key=lambda r: (predict(models[(r["shape"][0], r["name"])], r), r["config"]))
         best = min(rs, key=lambda r: r["us"])
         dflt = [r for r in rs if r["default"]][0]
-        out.append((sh, pick["us"], best["us"], dflt["us"], pick["config"], best["config"]))
+        out.append((sh, pick["us"], best["us"], dflt["us"], pick["name"], best["name"]))
     return out
 
 
@@ -207,7 +207,8 @@ def main():
     lines += summary_lines("held-out shapes:", ev_v) + [""]
     lines.append("held-out shapes, one by one (us: model's pick / fastest / sweep-time default):")
     for sh, mu, bu, du, pc, bc in ev_v:
-        lines.append("  %-60s %9.2f %9.2f %9.2f  cfg %2d (fastest %2d)" % (sh, mu, bu, du, pc, bc))
+        lines.append("  %-60s %9.2f %9.2f %9.2f  %s%s" % (sh, mu, bu, du, pc,
+                                                         "" if pc == bc else " (fastest: %s)" % bc))
     lines += ["", "per-configuration fit (shapes, occupancy, relative rms error):"]
     for (dt, name), n, occ, res in fits:
         lines.append("  %-4s %-80s %4d %2d %6.3f" % (dt, name[:80], n, occ, res))

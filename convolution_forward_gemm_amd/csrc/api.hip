@@ -240,6 +240,7 @@ bool plan(conv2d_fprop_desc_s &d, int cfg) {
     const F32Config &c = kF32Configs[cfg];
     if (f32_lds_bytes(d, cfg) > 160 * 1024) return false;
     if (c.max_rs > 0 && d.R * d.S > c.max_rs) return false;
+    if (c.nk > 0 && ((int64_t)d.C * d.R * d.S + 1) / 2 != c.nk) return false;
     const int64_t mt = (M + c.bn - 1) / c.bn, kt = (d.K + c.bm - 1) / c.bm;
     if (mt * kt > 0x7fffffff) return false;
     F32Params &p = d.f32;

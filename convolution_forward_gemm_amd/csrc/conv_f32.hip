@@ -284,6 +284,100 @@ static hipError_t launch_f32(const float *x, const float *w, float *y,
         DB ? 64 * F32Tile<FK, FP, CC, DEPTH, NW, DB>::MAXJ / CC : 0,                  \
         &launch_f32<FK, FP, CC, DEPTH, NW, DB>                                         \
   }
+// Tiny problems (a reduction of at most a few dozen MFMA steps, e.g. the
+// first layer of a network on 3 input channels): one wave per 32-channel x
+// 32-pixel tile loads every step's filter and pixel values straight into
+// registers -- all before the first MFMA -- and runs the NK MFMAs with two
+// accumulator chains.  Reduction index j = 2*step + (lane / 32) walks
+// (c, r, s) in KCRS order; each lane advances its own (c, r, s) by two per
+// step.  Indices past C*R*S, channels past K, pixels past M and padding read
+// zeros.  fp32 sums in a different order than the staged kernel: the result
+// obeys the same tolerance.
+template <int NK>
+__global__ void __launch_bounds__(64)
+conv_f32_tiny_kernel(const float *__restrict__ x, const float *__restrict__ w,
+                     float *__restrict__ y, F32Params p) {
+  const int lane = threadIdx.x;
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+  const int ktile = blockIdx.x % p.k_tiles;
+  const int mtile = blockIdx.x / p.k_tiles;
+  const int k0 = ktile * 32, m0 = mtile * 32;
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, p.x_bytes);
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(w, p.w_bytes);
+  const int RS = p.R * p.S, CRS = p.C * RS;
+
+  int h0 = -0x40000000, w0 = -0x40000000, xbase = 0;
+  const int m = m0 + l32;
+  if (m < p.M) {
+    const int n = m / p.PQ;
+    const int pq = m - n * p.PQ;
+    const int op = pq / p.Q;
+    const int oq = pq - op * p.Q;
+    h0 = op * p.sh - p.ph;
+    w0 = oq * p.sw - p.pw;
+    xbase = n * p.C * p.HW;
+  }
+  const int k = k0 + l32;
+  const bool kok = k < p.K;
+  const uint32_t wrow = (uint32_t)(k * CRS);
+  // this lane's reduction index j = half at step 0
+  int c = 0, r = 0, s = 0;
+  auto adv = [&]() {
+    if (++s == p.S) {
+      s = 0;
+      if (++r == p.R) {
+        r = 0;
+        ++c;
+      }
+    }
+  };
+  if (half) adv();
+  float a[NK], b[NK];
+#pragma unroll
+  for (int g = 0; g < NK; ++g) {
+    const int j = 2 * g + half;
+    const bool jok = j < CRS;
+    a[g] = load_f32(wr, (kok & jok) ? (wrow + j) * 4u : OOB_OFFSET);
+    const int h = h0 + r * p.dh, ww = w0 + s * p.dw;
+    const bool ok = jok & ((unsigned)h < (unsigned)p.H) & ((unsigned)ww < (unsigned)p.W);
+    b[g] = load_f32(xr, ok ? (uint32_t)(xbase + c * p.HW + h * p.W + ww) * 4u : OOB_OFFSET);
+    adv();
+    adv();
+  }
+  __builtin_amdgcn_sched_barrier(0);  // every load before the first MFMA
+  v16f acc[2] = {v16f{0.0f}, v16f{0.0f}};
+#pragma unroll
+  for (int g = 0; g < NK; ++g)
+    acc[g & 1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[g], b[g], acc[g & 1], 0, 0, 0);
+  // epilogue as in conv_f32_kernel: register i holds channel
+  // 8*(i/4) + 4*half + i%4 of pixel l32
+  if (m < p.M) {
+    const int n = m / p.PQ;
+    const int pq = m - n * p.PQ;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int kk = k0 + 8 * (i / 4) + 4 * half + (i % 4);
+      if (kk < p.K) {
+        const float sum = acc[0][i] + acc[1][i];
+        float v = (p.alpha_k ? p.alpha_k[kk] : p.alpha) * sum;
+        if (p.bias_k) v = v + p.bias_k[kk];
+        y[((size_t)n * p.K + kk) * p.PQ + pq] = v;
+      }
+    }
+  }
+}
+
+template <int NK>
+static hipError_t launch_f32_tiny(const float *x, const float *w, float *y, const F32Params &p,
+                                  int grid, hipStream_t s) {
+  hipLaunchKernelGGL((conv_f32_tiny_kernel<NK>), dim3(grid), dim3(64), 0, s, x, w, y, p);
+  return hipGetLastError();
+}
+
+#define F32_TINY_CFG(NK) \
+  F32Config { "f32_tiny_unrolled_steps" #NK "_mfma32x32x2_frag1x1", 32, 32, 64, 0, 0, &launch_f32_tiny<NK>, NK }
+
 #define F32_CFG(FK, FP, CC, DEPTH) \
   F32_CFG_W(FK, FP, CC, DEPTH, 4, 0, "f32_mfma32x32x2_frag" #FK "x" #FP "_cc" #CC "_depth" #DEPTH)
 #define F32_CFG16(FK, FP, CC, DEPTH) \
@@ -313,6 +407,9 @@ F32Config kF32Configs[] = {
     // 16 waves keeps four per SIMD; an 8-wave workgroup with two buffers
     // drops to two waves per SIMD and runs 7% slower than config 5.
     F32_CFG16_DB(2, 2, 4, 3),
+    // tiny problems, exactly NK = ceil(C*R*S / 2) MFMA steps (on 3 input
+    // channels: 1x1, 3x3, 5x5, 5x9, 7x7)
+    F32_TINY_CFG(2), F32_TINY_CFG(14), F32_TINY_CFG(38), F32_TINY_CFG(68), F32_TINY_CFG(74),
 };
 int kNumF32Configs = sizeof(kF32Configs) / sizeof(kF32Configs[0]);
 

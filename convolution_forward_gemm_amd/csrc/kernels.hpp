@@ -90,6 +90,8 @@ struct F32Config {
   int max_rs;   // largest R*S it runs (double-buffered staging holds a chunk
                 // in registers), 0 = any
   F32LaunchFn launch;
+  int nk;       // > 0: runs only problems of exactly nk MFMA steps,
+                // ceil(C*R*S / 2) (the unrolled tiny kernel)
 };
 
 extern F32Config kF32Configs[];

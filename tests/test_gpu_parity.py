@@ -296,6 +296,12 @@ F32_CASES = [
     (3, 3, 9, 30, 17, 2, 4, (0, 2), (2, 3), (3, 1)),
     (1, 8, 1, 1, 8, 1, 1, (0, 0), (1, 1), (1, 1)),
     (2, 16, 33, 7, 96, 3, 1, (1, 0), (1, 2), (1, 1)),
+    # three input channels: the tiny kernels' step counts (2, 14, 38, 68, 74)
+    (3, 3, 9, 8, 33, 1, 1, (0, 0), (1, 1), (1, 1)),
+    (2, 3, 17, 19, 40, 3, 3, (1, 1), (1, 1), (1, 1)),
+    (1, 3, 23, 21, 64, 5, 5, (2, 2), (2, 2), (1, 1)),
+    (2, 3, 25, 40, 20, 5, 9, (2, 4), (1, 1), (2, 3)),
+    (1, 3, 30, 30, 48, 7, 7, (3, 3), (2, 2), (1, 1)),
 ]
 
 

@@ -266,6 +266,11 @@ def grid_shapes(kind):
                     for H, W in ((64, 64), (256, 256), (128, 200)):
                         for R, S, ph, pw, sh, sw, dh, dw in _FILTERS_F32:
                             out.append(("fp32", N, C, H, W, K, R, S, ph, pw, sh, sw, dh, dw))
+        # a network's first layer: 7x7 stride 2 on three channels
+        for N in (1, 8, 32):
+            for H in (112, 224):
+                for K in (32, 64):
+                    out.append(("fp32", N, 3, H, H, K, 7, 7, 3, 3, 2, 2, 1, 1))
     elif kind == "validate":
         out += [("int8", 4, 256, 28, 28, 256, 3, 3, 1, 1, 1, 1, 1, 1),    # 3x3 C256 share, N/8
                 ("int8", 4, 128, 56, 56, 256, 3, 3, 1, 1, 2, 2, 1, 1),    # stride-2 share, N/8
@@ -314,7 +319,7 @@ def _median_us(torch, fn, target_us=300.0, reps=3):
     return ts[len(ts) // 2]
 
 
-def run_shape_grid(kind, out_path, only=None):
+def run_shape_grid(kind, out_path, only=None, skip_known=None):
     """Time every configuration that runs each shape of the grid (or only the
     named ones); one JSON line per (shape, configuration) appended to
     out_path."""
@@ -322,6 +327,10 @@ def run_shape_grid(kind, out_path, only=None):
     from . import binding as b
 
     shapes = grid_shapes(kind)
+    if skip_known:  # only the shapes a kept sweep does not hold yet
+        from .fit_select import load
+        known = {tuple(r["shape"]) for r in load(skip_known)}
+        shapes = [sh for sh in shapes if tuple(sh) not in known]
     s = torch.cuda.current_stream().cuda_stream
     # steady clock first: ~0.1 s of back-to-back work
     wc = b.Conv2dFprop(32, 256, 28, 28, 256, 3, 3, pad=1)
@@ -387,9 +396,11 @@ def main():
     ap.add_argument("--grid", choices=["train", "validate"], help="time a shape grid (model fit)")
     ap.add_argument("--out", help="with --grid: JSON-lines output file")
     ap.add_argument("--only", help="with --grid: comma-separated configuration names to time")
+    ap.add_argument("--skip-known", metavar="CSV_GZ",
+                    help="with --grid: skip the shapes this kept sweep already holds")
     a = ap.parse_args()
     if a.grid:
-        run_shape_grid(a.grid, a.out, set(a.only.split(",")) if a.only else None)
+        run_shape_grid(a.grid, a.out, set(a.only.split(",")) if a.only else None, a.skip_known)
         return
     if a.summarize_trace:
         print(summarize_trace(a.workload, a.summarize_trace, a.command, a.out_dir, a.sweep_log))

@@ -290,6 +290,10 @@ def grid_shapes(kind):
                   int(rng.integers(16, 300)), 16 * int(rng.integers(1, 9))) + f
             if _shape_ok(sh):
                 out.append(sh)
+        # three-channel first layers (the tiny fp32 kernels' domain)
+        out += [("fp32", 2, 3, 96, 150, 48, 3, 3, 1, 1, 1, 1, 1, 1),
+                ("fp32", 4, 3, 160, 160, 64, 7, 7, 3, 3, 2, 2, 1, 1),
+                ("fp32", 1, 3, 300, 200, 32, 5, 5, 2, 2, 1, 1, 1, 1)]
     else:
         raise ValueError(kind)
     return [sh for sh in out if _shape_ok(sh)]

@@ -122,6 +122,7 @@ def gpu_conv_f32_scaled(x, w, alpha, bias, pad, stride, dil, config=None):
 F32_CASES = [
     (2, 5, 13, 11, 40, 3, 3, (1, 1), (1, 1), (1, 1)),
     (1, 32, 20, 24, 64, 5, 9, (2, 4), (1, 1), (2, 3)),
+    (2, 3, 17, 19, 40, 3, 3, (1, 1), (1, 1), (1, 1)),      # three channels (unrolled tiny)
 ]
 
 

@@ -752,6 +752,9 @@ I8Config kI8HaloConfigs[] = {
     I8_HALO_AD_CFG(2, 2, 2, 1, 3, 3, 4, 2, 32, 1),
     I8_HALO_AD_CFG(2, 2, 1, 1, 3, 3, 3, 4, 64, 1),
     I8_HALO_AD_CFG(2, 2, 1, 2, 3, 3, 3, 6, 64, 1),
+    // the same with room for stride-2 halos (rows twice as far apart)
+    I8_HALO_AD_CFG(2, 2, 1, 1, 3, 3, 3, 6, 64, 1),
+    I8_HALO_AD_CFG(2, 2, 1, 2, 3, 3, 3, 9, 64, 1),
 };
 int kNumI8HaloConfigs = sizeof(kI8HaloConfigs) / sizeof(kI8HaloConfigs[0]);
 

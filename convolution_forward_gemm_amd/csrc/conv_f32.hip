@@ -46,7 +46,9 @@ struct F32Tile {
   static_assert(THREADS % 64 == 0 && BM % (THREADS / 64) == 0, "staging rows per pass");
 };
 
-template <int FK, int FP, int CC, int DEPTH, int NW, int DB>
+// FULLC: C is a multiple of CC, so every chunk holds CC channels and the
+// activation loads take the once-per-pixel mask (instantiated per launch).
+template <int FK, int FP, int CC, int DEPTH, int NW, int DB, bool FULLC>
 __global__ void __launch_bounds__(64 * NW)
 conv_f32_kernel(const float *__restrict__ x, const float *__restrict__ w,
                 float *__restrict__ y, F32Params p) {
@@ -116,6 +118,11 @@ conv_f32_kernel(const float *__restrict__ x, const float *__restrict__ w,
       }
     }
   };
+  // LDS row of weight j = cc*R*S + tap of a chunk: rows go tap-major
+  // ([r][s][cc][k]), so the channel-pair stride of the MFMA operand reads is
+  // a compile-time constant (immediate offsets) and one add per tap moves
+  // them to the next tap
+  auto wrow = [&](int j) { return (j % RS) * CC + j / RS; };
   auto wstore = [&](float *buf) {
     const int jl = tid & 63;
     const int kr = tid >> 6;
@@ -124,7 +131,7 @@ conv_f32_kernel(const float *__restrict__ x, const float *__restrict__ w,
       const int j = ji * 64 + jl;
       if (j < crs) {
 #pragma unroll
-        for (int ki = 0; ki < (DB ? T::KI : 1); ++ki) buf[j * T::LDP + kr + ki * T::ROWS] = wnext[ji][ki];
+        for (int ki = 0; ki < (DB ? T::KI : 1); ++ki) buf[wrow(j) * T::LDP + kr + ki * T::ROWS] = wnext[ji][ki];
       }
     }
   };
@@ -149,12 +156,13 @@ conv_f32_kernel(const float *__restrict__ x, const float *__restrict__ w,
       for (int j0 = 0; j0 < crs; j0 += 64) {
         const int j = j0 + jl;
         const int c = c0 + j / RS;
+        const int row = wrow(j);
 #pragma unroll 4
         for (int kk = kr; kk < T::BM; kk += ROWS) {
           const int k = k0 + kk;
           float v = 0.0f;
           if (j < crs && k < p.K && c < p.C) v = w[((size_t)k * p.C + c0) * RS + j];
-          if (j < crs) wl[j * T::LDP + kk] = v;
+          if (j < crs) wl[row * T::LDP + kk] = v;
         }
       }
     __syncthreads();
@@ -176,7 +184,11 @@ conv_f32_kernel(const float *__restrict__ x, const float *__restrict__ w,
     }
     float ring[DEPTH][T::PAIRS][FP];
     int ld_r = 0, ld_s = 0, ld_tap = 0;
-    auto load_next = [&](float (&dst)[T::PAIRS][FP]) {
+    // With every channel of the chunk present (FULL) a lane masks its pixel
+    // once per tap and the channel pair's plane offset rides in the
+    // wave-uniform soffset; otherwise each (pixel, pair) is masked.
+    auto load_next = [&](float (&dst)[T::PAIRS][FP], auto full_c) {
+      constexpr bool FULL = decltype(full_c)::value;
       const bool live = ld_tap < RS;
       const int rdh = ld_r * p.dh, sdw = ld_s * p.dw;
 #pragma unroll
@@ -186,9 +198,17 @@ conv_f32_kernel(const float *__restrict__ x, const float *__restrict__ w,
         // bitwise, not short-circuit, so that no branch is formed
         const bool ok = live & ((unsigned)h < (unsigned)p.H) & ((unsigned)ww < (unsigned)p.W);
         const uint32_t base = (uint32_t)(px_base[b] + rdh * p.W + sdw);
+        if constexpr (FULL) {
+          const uint32_t vo = ok ? (base + (uint32_t)(half * p.HW)) * 4u : OOB_OFFSET;
 #pragma unroll
-        for (int i = 0; i < T::PAIRS; ++i)
-          dst[i][b] = load_f32(xr, (ok & chan_ok[i]) ? (base + chan_off[i]) * 4u : OOB_OFFSET);
+          for (int i = 0; i < T::PAIRS; ++i)
+            dst[i][b] = __builtin_bit_cast(
+                float, __builtin_amdgcn_raw_buffer_load_b32(xr, vo, (c0 + 2 * i) * p.HW * 4, 0));
+        } else {
+#pragma unroll
+          for (int i = 0; i < T::PAIRS; ++i)
+            dst[i][b] = load_f32(xr, (ok & chan_ok[i]) ? (base + chan_off[i]) * 4u : OOB_OFFSET);
+        }
       }
       ++ld_tap;
       if (++ld_s == p.S) {
@@ -197,11 +217,12 @@ conv_f32_kernel(const float *__restrict__ x, const float *__restrict__ w,
       }
     };
 
+    const bool has_next = c0 + CC < p.C;
+    auto taps = [&](auto full_c) {
 #pragma unroll
-    for (int d = 0; d < DEPTH - 1; ++d) load_next(ring[d]);
+    for (int d = 0; d < DEPTH - 1; ++d) load_next(ring[d], full_c);
     // DB: the next chunk's weights go out behind the first activation taps,
     // a whole chunk ahead of their use
-    const bool has_next = c0 + CC < p.C;
     if (DB && has_next) wload(c0 + CC);
 
     const int rs_blocks = (RS + DEPTH - 1) / DEPTH;
@@ -212,7 +233,7 @@ conv_f32_kernel(const float *__restrict__ x, const float *__restrict__ w,
         // prefetch DEPTH-1 taps ahead into the slot freed last step; the
         // scheduling barrier keeps the loads at the head of the tap (the
         // scheduler would otherwise sink them next to their use)
-        load_next(ring[(d + DEPTH - 1) % DEPTH]);
+        load_next(ring[(d + DEPTH - 1) % DEPTH], full_c);
         __builtin_amdgcn_sched_barrier(0);
         const int ttw = tt < RS ? tt : RS - 1;
 #pragma unroll
@@ -220,7 +241,7 @@ conv_f32_kernel(const float *__restrict__ x, const float *__restrict__ w,
           float af[FK];
 #pragma unroll
           for (int a = 0; a < FK; ++a)
-            af[a] = wcur[((2 * i + half) * RS + ttw) * T::LDP + 32 * a + l32];
+            af[a] = wcur[(ttw * CC + 2 * i + half) * T::LDP + 32 * a + l32];
 #pragma unroll
           for (int a = 0; a < FK; ++a)
 #pragma unroll
@@ -230,6 +251,10 @@ conv_f32_kernel(const float *__restrict__ x, const float *__restrict__ w,
         }
       }
     }
+    };
+    // one variant per kernel: two copies of the tap loop in one kernel
+    // would raise its register use past the occupancy the tiles assume
+    taps(std::integral_constant<bool, FULLC>{});
     if constexpr (DB) {
       // the other buffer was last read in the previous chunk, before the
       // barrier that ended it
@@ -268,12 +293,20 @@ static hipError_t launch_f32(const float *x, const float *w, float *y,
                              const F32Params &p, int grid, hipStream_t s) {
   using T = F32Tile<FK, FP, CC, DEPTH, NW, DB>;
   const int lds = CC * p.R * p.S * T::LDP * 4 * (DB ? 2 : 1);
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void *>(&conv_f32_kernel<FK, FP, CC, DEPTH, NW, DB>),
+  static const hipError_t attr_full = hipFuncSetAttribute(
+      reinterpret_cast<const void *>(&conv_f32_kernel<FK, FP, CC, DEPTH, NW, DB, true>),
       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-  if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((conv_f32_kernel<FK, FP, CC, DEPTH, NW, DB>), dim3(grid),
-                     dim3(T::THREADS), lds, s, x, w, y, p);
+  static const hipError_t attr_part = hipFuncSetAttribute(
+      reinterpret_cast<const void *>(&conv_f32_kernel<FK, FP, CC, DEPTH, NW, DB, false>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  if (attr_full != hipSuccess) return attr_full;
+  if (attr_part != hipSuccess) return attr_part;
+  if (p.C % CC == 0)
+    hipLaunchKernelGGL((conv_f32_kernel<FK, FP, CC, DEPTH, NW, DB, true>), dim3(grid),
+                       dim3(T::THREADS), lds, s, x, w, y, p);
+  else
+    hipLaunchKernelGGL((conv_f32_kernel<FK, FP, CC, DEPTH, NW, DB, false>), dim3(grid),
+                       dim3(T::THREADS), lds, s, x, w, y, p);
   return hipGetLastError();
 }
 

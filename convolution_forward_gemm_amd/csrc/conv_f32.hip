@@ -182,6 +182,9 @@ conv_f32_kernel(const float *__restrict__ x, const float *__restrict__ w,
       chan_ok[i] = c < p.C;
       chan_off[i] = (uint32_t)(c * p.HW);
     }
+    uint32_t px_vo[FP];
+#pragma unroll
+    for (int b = 0; b < FP; ++b) px_vo[b] = (uint32_t)(px_base[b] + half * p.HW) * 4u;
     float ring[DEPTH][T::PAIRS][FP];
     int ld_r = 0, ld_s = 0, ld_tap = 0;
     // With every channel of the chunk present (FULL) a lane masks its pixel
@@ -197,14 +200,16 @@ conv_f32_kernel(const float *__restrict__ x, const float *__restrict__ w,
         const int ww = px_w0[b] + sdw;
         // bitwise, not short-circuit, so that no branch is formed
         const bool ok = live & ((unsigned)h < (unsigned)p.H) & ((unsigned)ww < (unsigned)p.W);
-        const uint32_t base = (uint32_t)(px_base[b] + rdh * p.W + sdw);
         if constexpr (FULL) {
-          const uint32_t vo = ok ? (base + (uint32_t)(half * p.HW)) * 4u : OOB_OFFSET;
+          // byte offset: the pixel's own part (channel c0 + half folded in)
+          // plus the tap's wave-uniform part; uint32 wrap-around is exact
+          const uint32_t vo = ok ? px_vo[b] + (uint32_t)(rdh * p.W + sdw) * 4u : OOB_OFFSET;
 #pragma unroll
           for (int i = 0; i < T::PAIRS; ++i)
             dst[i][b] = __builtin_bit_cast(
                 float, __builtin_amdgcn_raw_buffer_load_b32(xr, vo, (c0 + 2 * i) * p.HW * 4, 0));
         } else {
+          const uint32_t base = (uint32_t)(px_base[b] + rdh * p.W + sdw);
 #pragma unroll
           for (int i = 0; i < T::PAIRS; ++i)
             dst[i][b] = load_f32(xr, (ok & chan_ok[i]) ? (base + chan_off[i]) * 4u : OOB_OFFSET);

@@ -41,6 +41,11 @@ MUTANTS = {
     "per_channel_wrong_channel": ("volatile float g = f * alpha[k];", "volatile float g = f * alpha[(k + 1) % K];"),
     "per_channel_fused": ("volatile float g = f * alpha[k];\n                volatile float h = g + (bias ? bias[k] : 0.0f);",
                           "volatile float g = 0.0f;\n                volatile float h = fmaf(f, alpha[k], bias ? bias[k] : 0.0f) + g;"),
+    "f32_dropped_alpha": ("y[i] = (float)((double)alpha * acc[i]);", "y[i] = (float)acc[i];"),
+    "f32_acc_rounded_before_alpha": ("y[i] = (float)((double)alpha * acc[i]);",
+                                     "y[i] = (float)((double)alpha * (double)(float)acc[i]);"),
+    "f32_alpha_in_fp32": ("y[i] = (float)((double)alpha * acc[i]);",
+                          "y[i] = (float)acc[i] * alpha;"),
     "layout_hw_swapped": ("dst[((((size_t)n * (C / 32) + c / 32) * H + h) * W + w) * 32 + c % 32] =",
                           "dst[((((size_t)n * (C / 32) + c / 32) * W + w) * H + h) * 32 + c % 32] ="),
     "filter_layout_rs_swapped": ("dst[((((size_t)(c / 32) * R + r) * S + s) * K + k) * 32 + c % 32] =",
@@ -71,6 +76,8 @@ def _battery():
         ("per_channel_c1", pins.test_per_channel_c1_all_ones_with_bias, ()),
         ("per_channel_scalar", pins.test_per_channel_with_one_scale_is_the_scalar_epilogue, ()),
         ("f32_per_channel_hand", pins.test_f32_per_channel_hand_values, ()),
+        ("f32_alpha_hand", pins.test_f32_epilogue_alpha_hand_values, ()),
+        ("f32_alpha_tap_trace", pins.test_f32_alpha_scales_the_tap_trace, ()),
     ]
     for acc, alpha, expect in [(2088960, 2.0 ** -14, 127), (-2105344, 2.0 ** -14, -128),
                                (40960, 2.0 ** -14, 2), (25, 0.1, 2)]:

@@ -349,6 +349,49 @@ def test_f32_integer_valued_exact_and_equal_to_int8_path():
 
 
 # --------------------------------------------------------------------------
+# fp32 output scale alpha: y = fl32(alpha * acc), one rounding of the exact
+# product of the fp32 alpha and the double accumulator
+# --------------------------------------------------------------------------
+def test_f32_epilogue_alpha_hand_values():
+    # Exact products (no rounding at all): 3/8 * 896 = 336, 3/8 * -7 = -2.625,
+    # 3/8 * 1e6 = 375000; -5/2 * 896 = -2240, -5/2 * -7 = 17.5.
+    y = oracle.epilogue_f32(np.array([896.0, -7.0, 1e6]), 0.375)
+    assert y.tolist() == [336.0, -2.625, 375000.0]
+    y = oracle.epilogue_f32(np.array([896.0, -7.0]), -2.5)
+    assert y.tolist() == [-2240.0, 17.5]
+    # One rounding, in the right place.  acc = 1 + 2^-24 + 2^-40 (exact in
+    # double, between the floats 1 and 1 + 2^-23), alpha = 3:
+    #   alpha * acc = 3 + 0.75 * 2^-22 + 3 * 2^-40; the floats in [2, 4) are
+    #   2^-22 apart, so the nearest is 3 + 2^-22.
+    # Rounding acc to fp32 first would give (1 + 2^-23) * 3 = 3 + 1.5 * 2^-22,
+    # a tie between 3 + 2^-22 (odd mantissa) and 3 + 2^-21 (even): 3 + 2^-21.
+    acc = 1.0 + 2.0 ** -24 + 2.0 ** -40
+    y = oracle.epilogue_f32(np.array([acc, -acc]), 3.0)
+    assert y.tolist() == [3.0 + 2.0 ** -22, -(3.0 + 2.0 ** -22)]
+    # The same with a non-dyadic alpha: fl32(0.1) = 13421773 * 2^-27.
+    # acc = 10 exactly: 10 * 13421773 * 2^-27 = 134217730 * 2^-27
+    # = 1.0000000149..., whose neighbours in [1, 2) are 1 and 1 + 2^-23 =
+    # 1.000000119...; the nearest is 1.0.
+    y = oracle.epilogue_f32(np.array([10.0]), 0.1)
+    assert y.tolist() == [1.0]
+
+
+def test_f32_alpha_scales_the_tap_trace():
+    # The transcript's trace of output (0,0,0,0) on all-ones data gives
+    # acc = C * 4 rows * 7 columns = 896 (pinned above); with alpha = -2.5 the
+    # output is -2240 exactly, and with alpha = 0.375 it is 336.
+    # A 24 x 24 input holds every traced tap of output (0, 0), so that output
+    # is the same as on the transcript's 512 x 512 image.
+    g = _golden("tap_trace_origin.json")
+    pr = g["problem"]
+    x = np.ones((1, pr["C"], 24, 24), np.float32)
+    w = np.ones((2, pr["C"], pr["R"], pr["S"]), np.float32)
+    for alpha, expect in ((-2.5, -2240.0), (0.375, 336.0)):
+        _, y = oracle.conv2d_f32(x, w, alpha, pad=pr["pad"], dil=pr["dil"])
+        assert y[0, 0, 0, 0] == expect and y[0, 1, 0, 0] == expect
+
+
+# --------------------------------------------------------------------------
 # Metamorphic properties
 # --------------------------------------------------------------------------
 def test_linearity_in_w_and_k_permutation():

@@ -259,6 +259,33 @@ def test_run_errors_leave_output_untouched():
     assert bool((y == 5).all())
 
 
+def test_run_ignores_an_earlier_pending_hip_error():
+    # A failed HIP call of the caller (here hipSetDevice on a device that does
+    # not exist) leaves an error pending.  run reports the status of its own
+    # launch: CONV_OK, with a correct output.
+    import ctypes
+    _announce("int8 run after a pending HIP error")
+    b = _b()
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipSetDevice.argtypes = [ctypes.c_int]
+    hip.hipSetDevice.restype = ctypes.c_int
+    wk = wl.WORKLOADS["c1"]
+    x, w = wl.make_inputs(wk)
+    conv = b.Conv2dFprop(wk.N, wk.C, wk.H, wk.W, wk.K, wk.R, wk.S, pad=wk.pad,
+                         stride=wk.stride, dil=wk.dil)
+    x_il = b.nchw_to_nc32hw32(_dev(x))
+    w_il = b.kcrs_to_c32rsk32(_dev(w))
+    y = torch.full(conv.y_shape, 77, dtype=torch.int8, device="cuda")
+    torch.cuda.synchronize()
+    assert hip.hipSetDevice(4096) != 0  # hipErrorInvalidDevice, now pending
+    st = b.lib.conv2d_fprop_run(conv._h, x_il.data_ptr(), w_il.data_ptr(), y.data_ptr(),
+                                wk.alpha, torch.cuda.current_stream().cuda_stream)
+    assert st == b.CONV_OK
+    torch.cuda.synchronize()
+    _, ref = oracle_i8_il(x, w, wk.alpha, wk.pad, wk.stride, wk.dil)
+    assert np.array_equal(y.cpu().numpy(), ref)
+
+
 # --------------------------------------------------------------------------
 # fp32
 # --------------------------------------------------------------------------
@@ -331,6 +358,68 @@ def test_f32_integer_valued_exact(case):
         y, _ = gpu_conv_f32(x, w, pad, stride, dil, config=cfg)
         assert np.array_equal(y.astype(np.float64), ref)
     each_config("fp32", run)
+
+
+# alpha != 1: the oracle's epilogue rounds fl32(alpha * acc) once from its
+# double accumulator; the kernel multiplies its fp32 accumulator by alpha.
+# Gaussian inputs: the tolerance rule.  Integer-valued inputs: the fp32
+# accumulator is exact, so both sides round the same exact product once and
+# must agree bit for bit.
+F32_ALPHAS = (0.37, -2.5)
+
+
+@pytest.mark.parametrize("case", F32_CASES)
+def test_f32_configs_alpha(case):
+    N, C, H, W, K, R, S, pad, stride, dil = case
+    x, w = wl.make_custom("fp32", N, C, H, W, K, R, S, seed=(hash(case) + 1) % 1000)
+    acc = oracle.conv2d_f32_acc(x, w, pad=pad, stride=stride, dil=dil, nthreads=NTHREADS)
+    refs = {a: oracle.epilogue_f32(acc, a) for a in F32_ALPHAS}
+
+    def run(cfg):
+        for a in F32_ALPHAS:
+            _announce("fp32 alpha", a, case, "config", cfg)
+            y, _ = gpu_conv_f32(x, w, pad, stride, dil, alpha=a, config=cfg)
+            assert_f32_rule(y, refs[a])
+    each_config("fp32", run)
+
+
+@pytest.mark.parametrize("case", F32_CASES)
+def test_f32_integer_valued_alpha_exact(case):
+    N, C, H, W, K, R, S, pad, stride, dil = case
+    r = np.random.default_rng((abs(hash(case)) + 5) % 1000)
+    x = r.integers(-1, 2, size=(N, C, H, W)).astype(np.float32)
+    w = r.integers(-1, 2, size=(K, C, R, S)).astype(np.float32)
+    acc = oracle.conv2d_f32_acc(x, w, pad=pad, stride=stride, dil=dil, nthreads=NTHREADS)
+    refs = {a: oracle.epilogue_f32(acc, a) for a in F32_ALPHAS}
+
+    def run(cfg):
+        for a in F32_ALPHAS:
+            _announce("fp32 alpha exact", a, case, "config", cfg)
+            y, _ = gpu_conv_f32(x, w, pad, stride, dil, alpha=a, config=cfg)
+            assert np.array_equal(y, refs[a])
+    each_config("fp32", run)
+
+
+def test_f32_workload_c5_slabs():
+    # Whole output slabs of the dilated 5x9 workload, element by element: all
+    # 64 output channels over the first 16 and the last 16 output rows of the
+    # first and the last image (2 x 64 x 32 x 496 = 2,031,616 outputs).  They
+    # hold complete 64-channel x 1024-pixel tiles of the chosen configuration,
+    # the top and bottom padding rows, and the ragged last tile of the output.
+    wk = wl.WORKLOADS["c5"]
+    _announce("fp32 workload c5 slabs", wk.name)
+    x, w = wl.make_inputs(wk)
+    y, conv = gpu_conv_f32(x, w, wk.pad, wk.stride, wk.dil, alpha=wk.alpha)
+    print("config:", conv.config, flush=True)
+    N, K, P, Q = y.shape
+    rows = list(range(16)) + list(range(P - 16, P))
+    n_i, k_i, p_i, q_i = np.meshgrid([0, N - 1], np.arange(K), rows, np.arange(Q), indexing="ij")
+    pts = np.stack([a.ravel() for a in (n_i, k_i, p_i, q_i)], axis=1).astype(np.int32)
+    acc = oracle.conv2d_f32_points(x, w, pts, **wk.conv_kwargs, nthreads=NTHREADS)
+    ref = oracle.epilogue_f32(acc, wk.alpha)
+    got = y[tuple(pts.T)]
+    assert_f32_rule(got, ref)
+    assert np.all(np.isfinite(y))
 
 
 def test_f32_workload_c5_sampled():

@@ -10,6 +10,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <tuple>
+#include <type_traits>
+
 namespace convfprop {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -62,6 +65,27 @@ __device__ __forceinline__ int xcd_remap(int b, int total) {
   int q = total / NXCD, r = total % NXCD;
   int x = b % NXCD, i = b / NXCD;
   return x * q + (x < r ? x : r) + i;
+}
+
+// Host side: launch one kernel and return the status of that launch alone.
+// hipLaunchKernel reports the launch's own outcome; reading hipGetLastError()
+// after a launch would instead return (and clear) an error that an earlier,
+// unrelated HIP call of the caller left pending, and misreport a launch that
+// was in fact enqueued.  The arguments are converted to the kernel's
+// parameter types and passed by address, as the launch API expects.
+template <typename... KArgs, typename... Args>
+inline hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t lds,
+                                hipStream_t stream, Args &&...args) {
+  static_assert(sizeof...(KArgs) == sizeof...(Args), "kernel argument count");
+  std::tuple<std::remove_cv_t<std::remove_reference_t<KArgs>>...> values(
+      std::forward<Args>(args)...);
+  return std::apply(
+      [&](auto &...v) {
+        void *argv[] = {static_cast<void *>(&v)...};
+        return hipLaunchKernel(reinterpret_cast<const void *>(kernel), grid, block, argv, lds,
+                               stream);
+      },
+      values);
 }
 
 }  // namespace convfprop

@@ -307,12 +307,10 @@ static hipError_t launch_f32(const float *x, const float *w, float *y,
   if (attr_full != hipSuccess) return attr_full;
   if (attr_part != hipSuccess) return attr_part;
   if (p.C % CC == 0)
-    hipLaunchKernelGGL((conv_f32_kernel<FK, FP, CC, DEPTH, NW, DB, true>), dim3(grid),
+    return launch_kernel(&conv_f32_kernel<FK, FP, CC, DEPTH, NW, DB, true>, dim3(grid),
+                         dim3(T::THREADS), lds, s, x, w, y, p);
+  return launch_kernel(&conv_f32_kernel<FK, FP, CC, DEPTH, NW, DB, false>, dim3(grid),
                        dim3(T::THREADS), lds, s, x, w, y, p);
-  else
-    hipLaunchKernelGGL((conv_f32_kernel<FK, FP, CC, DEPTH, NW, DB, false>), dim3(grid),
-                       dim3(T::THREADS), lds, s, x, w, y, p);
-  return hipGetLastError();
 }
 
 #define F32_CFG_W(FK, FP, CC, DEPTH, NW, DB, NAME)                                   \
@@ -409,8 +407,7 @@ conv_f32_tiny_kernel(const float *__restrict__ x, const float *__restrict__ w,
 template <int NK>
 static hipError_t launch_f32_tiny(const float *x, const float *w, float *y, const F32Params &p,
                                   int grid, hipStream_t s) {
-  hipLaunchKernelGGL((conv_f32_tiny_kernel<NK>), dim3(grid), dim3(64), 0, s, x, w, y, p);
-  return hipGetLastError();
+  return launch_kernel(&conv_f32_tiny_kernel<NK>, dim3(grid), dim3(64), 0, s, x, w, y, p);
 }
 
 #define F32_TINY_CFG(NK) \

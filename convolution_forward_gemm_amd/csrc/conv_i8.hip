@@ -406,9 +406,8 @@ static hipError_t launch_i8_pc(const int8_t *x, const int8_t *w, int8_t *y,
       reinterpret_cast<const void *>(&conv_i8_kernel<WK, WP, FK, FP, KT, NS, RSO, PC>),
       hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS_BYTES);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((conv_i8_kernel<WK, WP, FK, FP, KT, NS, RSO, PC>), dim3(grid),
+  return launch_kernel(&conv_i8_kernel<WK, WP, FK, FP, KT, NS, RSO, PC>, dim3(grid),
                      dim3(T::THREADS), T::LDS_BYTES, s, x, w, y, p);
-  return hipGetLastError();
 }
 
 // Launch with the per-output-channel epilogue when the call carries one.

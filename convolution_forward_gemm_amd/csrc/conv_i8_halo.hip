@@ -655,9 +655,8 @@ static hipError_t launch_i8_halo_ad_pc(const int8_t *x, const int8_t *w, int8_t 
       reinterpret_cast<const void *>(&conv_i8_halo_ad_kernel<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, PC>),
       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((conv_i8_halo_ad_kernel<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, PC>), dim3(grid),
+  return launch_kernel(&conv_i8_halo_ad_kernel<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, PC>, dim3(grid),
                      dim3(T::THREADS), p.lds_bytes, s, x, w, y, p);
-  return hipGetLastError();
 }
 
 template <int WK, int WP, int FK, int FP, int R, int S, int NS, int HJ, int PW, int CPS, int AL>
@@ -676,9 +675,8 @@ static hipError_t launch_i8_halo_pc(const int8_t *x, const int8_t *w, int8_t *y,
       reinterpret_cast<const void *>(&conv_i8_halo_kernel<WK, WP, FK, FP, R, S, NS, HJ, PC>),
       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((conv_i8_halo_kernel<WK, WP, FK, FP, R, S, NS, HJ, PC>), dim3(grid),
+  return launch_kernel(&conv_i8_halo_kernel<WK, WP, FK, FP, R, S, NS, HJ, PC>, dim3(grid),
                      dim3(T::THREADS), p.lds_bytes, s, x, w, y, p);
-  return hipGetLastError();
 }
 
 template <int WK, int WP, int FK, int FP, int R, int S, int NS, int HJ>

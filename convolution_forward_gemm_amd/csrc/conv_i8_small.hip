@@ -112,9 +112,8 @@ static hipError_t launch_i8_small_pc(const int8_t *x, const int8_t *w, int8_t *y
       reinterpret_cast<const void *>(&conv_i8_small_kernel<FP, PC>),
       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((conv_i8_small_kernel<FP, PC>), dim3(grid), dim3(64), p.lds_bytes, s, x, w, y,
+  return launch_kernel(&conv_i8_small_kernel<FP, PC>, dim3(grid), dim3(64), p.lds_bytes, s, x, w, y,
                      p);
-  return hipGetLastError();
 }
 
 template <int FP>
@@ -190,8 +189,7 @@ conv_i8_tiny_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ w,
 template <int R, int S, int CB, bool PC>
 static hipError_t launch_i8_tiny_pc(const int8_t *x, const int8_t *w, int8_t *y, const I8Params &p,
                                     int grid, hipStream_t s) {
-  hipLaunchKernelGGL((conv_i8_tiny_kernel<R, S, CB, PC>), dim3(grid), dim3(64), 0, s, x, w, y, p);
-  return hipGetLastError();
+  return launch_kernel(&conv_i8_tiny_kernel<R, S, CB, PC>, dim3(grid), dim3(64), 0, s, x, w, y, p);
 }
 
 template <int R, int S, int CB>
@@ -260,8 +258,7 @@ conv_i8_tinyn_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ w,
 template <int NT, bool PC>
 static hipError_t launch_i8_tinyn_pc(const int8_t *x, const int8_t *w, int8_t *y, const I8Params &p,
                                      int grid, hipStream_t s) {
-  hipLaunchKernelGGL((conv_i8_tinyn_kernel<NT, PC>), dim3(grid), dim3(64), 0, s, x, w, y, p);
-  return hipGetLastError();
+  return launch_kernel(&conv_i8_tinyn_kernel<NT, PC>, dim3(grid), dim3(64), 0, s, x, w, y, p);
 }
 
 template <int NT>

@@ -81,6 +81,32 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_host_sanitized(out: str, verbose: bool = False) -> str:
+    """The library with its host code built under AddressSanitizer and
+    UndefinedBehaviorSanitizer (descriptor creation, planning, the selection
+    model, argument checks, launchers); the gfx950 device code is built as
+    usual, unsanitized.  The sanitizer runtime is the shared one of the ROCm
+    clang, so a test program built by that clang with the same flags shares
+    it.  Written to `out`; the in-tree library is not touched."""
+    import concurrent.futures
+    import tempfile
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer",
+           "-Xarch_host", "-shared-libsan"]
+    cflags = [f for f in FLAGS if f != "-shared"] + ["-O1", "-g"] + san
+    with tempfile.TemporaryDirectory() as d:
+        def compile_one(src):
+            obj = os.path.join(d, src + ".o")
+            _run([HIPCC, *cflags, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+            return obj
+        workers = max(1, min(len(SOURCES), os.cpu_count() or 1))
+        with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
+            objs = list(ex.map(compile_one, SOURCES))
+        _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *san, *objs, "-o", out],
+             verbose)
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
     print(build_peak_probe(verbose=True))

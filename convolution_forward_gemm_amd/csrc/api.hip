@@ -42,6 +42,18 @@ int64_t out_extent(int64_t in, int64_t pad, int64_t dil, int64_t k, int64_t stri
   return num / stride + 1;
 }
 
+// The integer a C caller passed for an enum parameter.  C lets any int value
+// through an enum type; in C++ reading an enum object whose value lies
+// outside the enumerators' range is undefined, so the bits are copied out
+// instead of loading the enum.
+template <typename E>
+int enum_bits(const E &e) {
+  static_assert(sizeof(E) == sizeof(int), "C enums are int-sized");
+  int v;
+  memcpy(&v, &e, sizeof v);
+  return v;
+}
+
 bool ranges_overlap(const void *a, int64_t an, const void *b, int64_t bn) {
   const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
   return a0 < b0 + (uintptr_t)bn && b0 < a0 + (uintptr_t)an;
@@ -321,8 +333,8 @@ bool plan_by_model(conv2d_fprop_desc_s &d) {
 
 extern "C" {
 
-const char *conv_status_string(conv_status_t s) {
-  switch (s) {
+const char *conv_status_string(conv_status_t status) {
+  switch (enum_bits(status)) {
     case CONV_OK: return "CONV_OK: success";
     case CONV_ERR_NULL: return "CONV_ERR_NULL: a required pointer is NULL";
     case CONV_ERR_INVALID_SHAPE: return "CONV_ERR_INVALID_SHAPE: invalid sizes or empty output";
@@ -351,13 +363,14 @@ conv_status_t conv2d_fprop_desc_create(conv2d_fprop_desc_t *out, int N, int C,
   const int64_t Q = out_extent(W, pad_w, dil_w, S, stride_w);
   if (P < 1 || Q < 1) return CONV_ERR_INVALID_SHAPE;
 
+  const int dt = enum_bits(dtype), lay = enum_bits(layout);
   int64_t esize;
-  if (dtype == CONV_DTYPE_INT8 && layout == CONV_LAYOUT_NC32HW32_C32RSK32) {
+  if (dt == CONV_DTYPE_INT8 && lay == CONV_LAYOUT_NC32HW32_C32RSK32) {
     if (C % 32 != 0 || K % 32 != 0) return CONV_ERR_UNSUPPORTED;
     // |acc| <= C*R*S * 128 * 128 must stay below 2^31.
     if ((int64_t)C * R * S >= 131072) return CONV_ERR_OVERFLOW_RISK;
     esize = 1;
-  } else if (dtype == CONV_DTYPE_FP32 && layout == CONV_LAYOUT_NCHW_KCRS) {
+  } else if (dt == CONV_DTYPE_FP32 && lay == CONV_LAYOUT_NCHW_KCRS) {
     esize = 4;
   } else {
     return CONV_ERR_UNSUPPORTED;
@@ -420,8 +433,9 @@ conv_status_t conv2d_fprop_desc_get_config(conv2d_fprop_desc_t d, char *buf, siz
 }
 
 int conv2d_fprop_num_configs(conv_dtype_t dtype) {
-  if (dtype == CONV_DTYPE_INT8) return num_i8_configs();
-  if (dtype == CONV_DTYPE_FP32) return kNumF32Configs;
+  const int dt = enum_bits(dtype);
+  if (dt == CONV_DTYPE_INT8) return num_i8_configs();
+  if (dt == CONV_DTYPE_FP32) return kNumF32Configs;
   return 0;
 }
 

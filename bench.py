@@ -107,6 +107,24 @@ def time_device(torch, fn, steps, warmup):
     return start.elapsed_time(stop) / steps
 
 
+def clock_ramp(torch, fn, min_ms=60.0, batch=200):
+    """Sustained untimed load before any warm-up count: the GPU reaches its
+    steady clock only after tens of milliseconds under load, so a short
+    warm-up alone would time a still-ramping clock.  Launches fn in batches
+    until at least min_ms of wall time has passed; returns (ms, launches)."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        for _ in range(batch):
+            fn()
+        n += batch
+        torch.cuda.synchronize()
+        el = (time.perf_counter() - t0) * 1e3
+        if el >= min_ms:
+            return el, n
+
+
 def latency_suite(torch, conv, xd, wd, yd, alpha, calls=1000):
     """p5-style microseconds per call: device events, host wall, graph replay."""
     stream = torch.cuda.current_stream().cuda_stream
@@ -225,86 +243,6 @@ def cpu_baseline(wk, x, w):
 # ---------------------------------------------------------------------------
 # Summaries of rocprofv3 output (run on the host after the profiled runs)
 # ---------------------------------------------------------------------------
-def library_comparison(torch, b, wl):
-    """The same work through ROCm's own libraries on this GPU, for context.
-
-    int8: hipBLASLt through torch._int_mm on the explicit GEMM of each
-    problem (M = N*P*Q, reduction C*R*S, N = K) -- less work than the
-    convolution (no implicit im2col, no epilogue, int32 out), with the
-    faster of the two operand layouts.  fp32: MIOpen through
-    torch.nn.functional.conv2d on NCHW tensors, TF32 off (end to end: it
-    includes MIOpen's own layout transposes).  Times are device-event
-    averages on the current stream; ours run through run_ptr."""
-    import dataclasses
-    torch.backends.cudnn.allow_tf32 = False
-    stream = torch.cuda.current_stream().cuda_stream
-    rows = []
-    share = dataclasses.replace(wl.WORKLOADS["c3"], key="c3_n4", N=4,
-                                name="int8 conv2d fprop 3x3 N4 C256 H28 W28 K256 stride1 pad1")
-    for wk, calls in ((wl.WORKLOADS["c3"], 200), (wl.WORKLOADS["c4"], 200), (share, 400),
-                      (wl.WORKLOADS["c5"], 5)):
-        conv, xd, wd, yd, _ = setup(wk, torch, b)
-        xp, wp, yp = xd.data_ptr(), wd.data_ptr(), yd.data_ptr()
-        warm = 2000 if wk.dtype == "int8" else 3  # int8: let the clocks settle
-        ours_ms = time_device(torch, lambda: conv.run_ptr(xp, wp, yp, wk.alpha, stream), calls, warm)
-        ops = conv_ops(wk, conv.P, conv.Q)
-        row = {"workload": wk.name, "ours_us": round(ours_ms * 1e3, 2),
-               "ours_rate": round(ops / (ours_ms * 1e-3) / 1e12, 1), "ours_config": conv.config}
-        del xd, wd, yd
-        if wk.dtype == "int8":
-            M, Kr, Nn = wk.N * conv.P * conv.Q, wk.C * wk.R * wk.S, wk.K
-            g = torch.Generator(device="cuda")
-            g.manual_seed(7)
-            A = torch.randint(-128, 128, (M, Kr), dtype=torch.int8, device="cuda", generator=g)
-            Bt = torch.randint(-128, 128, (Nn, Kr), dtype=torch.int8, device="cuda", generator=g)
-            best = None
-            for name, B in (("B column-major", Bt.t()), ("B row-major", Bt.t().contiguous())):
-                ms = time_device(torch, lambda: torch._int_mm(A, B), calls, warm)
-                if best is None or ms < best[0]:
-                    best = (ms, name)
-            row.update({"library": "hipBLASLt int8 GEMM (torch._int_mm), %s, M=%d N=%d K=%d"
-                        % (best[1], M, Nn, Kr),
-                        "library_us": round(best[0] * 1e3, 2),
-                        "library_rate": round(ops / (best[0] * 1e-3) / 1e12, 1), "unit": "TOPS"})
-            del A, Bt
-        else:
-            x, w = wl.make_inputs(wk)
-            xt, wt = torch.from_numpy(x).cuda(), torch.from_numpy(w).cuda()
-            f = lambda: torch.nn.functional.conv2d(xt, wt, stride=wk.stride, padding=wk.pad,
-                                                   dilation=wk.dil)
-            ms = time_device(torch, f, calls, 3)
-            row.update({"library": "MIOpen fp32 conv (torch.nn.functional.conv2d, NCHW, TF32 off)",
-                        "library_us": round(ms * 1e3, 2),
-                        "library_rate": round(ops / (ms * 1e-3) / 1e12, 1), "unit": "TFLOP/s"})
-            del xt, wt
-        row["ours_over_library_time"] = round(row["ours_us"] / row["library_us"], 3)
-        rows.append(row)
-        torch.cuda.empty_cache()
-    return rows
-
-
-def summarize_library_trace(trace_dir, log_path, commands):
-    """Per-kernel durations of a --library-comparison run under rocprofv3
-    --kernel-trace, next to the run's own JSON lines."""
-    import collections
-    d = collections.defaultdict(list)
-    for r in _csv_rows(_find(trace_dir, "kernel_trace.csv")):
-        d[r["Kernel_Name"]].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
-    out = ["# ROCm libraries on the same work (context, not a target)", "",
-           "Commands:", ""] + ["    " + c for c in commands] + ["",
-           "Event-timed lines printed by the run (ours_over_library_time < 1: ours is faster):", ""]
-    with open(log_path) as f:
-        out += ["    " + l.strip() for l in f if l.startswith("{")]
-    out += ["", "Kernel trace, every kernel above 5 us (library kernels include the",
-            "search MIOpen runs on first use; medians are the steady state):", "",
-            "| kernel | dispatches | median us | min us |", "|---|---|---|---|"]
-    for k, v in sorted(d.items(), key=lambda kv: -sum(kv[1])):
-        v = sorted(v)
-        if v[len(v) // 2] > 5:
-            out.append("| `%s` | %d | %.2f | %.2f |" % (k[:110], len(v), v[len(v) // 2], v[0]))
-    return "\n".join(out) + "\n"
-
-
 def _csv_rows(path):
     import csv
     with open(path, newline="") as f:
@@ -444,11 +382,12 @@ def _tag(args):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # The GPU clock ramps up over tens of milliseconds of sustained load: 50
-    # warm-up launches (~1 ms) leave the timed region ~12% slower than the
-    # steady state that 3000 (~50 ms) reach.
+    # The GPU clock ramps up over tens of milliseconds of sustained load;
+    # every run first spends at least --clock-ramp-ms of untimed launches of
+    # the timed step (reported as clock_ramp_ms), whatever --warmup is.
     ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=3000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--clock-ramp-ms", type=float, default=60.0)
     ap.add_argument("--no-extras", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--workload", default="c3", help="headline workload key (c3 default)")
@@ -466,19 +405,12 @@ def main():
                          "output directories of this script, then exit")
     ap.add_argument("--command", action="append", default=[],
                     help="with --summarize-*: the profiling command(s) to record")
-    ap.add_argument("--library-comparison", action="store_true",
-                    help="time hipBLASLt / MIOpen on the same work and print those lines only")
-    ap.add_argument("--summarize-library-trace", nargs=2, metavar=("TRACE_DIR", "LOG"),
-                    help="summary of a --library-comparison run under rocprofv3 --kernel-trace")
     ap.add_argument("--config", type=int, default=None,
                     help="run another compiled configuration of the workload (for profiling "
                          "alternatives; summaries then carry a _cfg<N> suffix)")
     args = ap.parse_args()
     if args.summarize_counters:
         print(summarize_counters(args.workload, args.summarize_counters, args.command, _tag(args)))
-        return
-    if args.summarize_library_trace:
-        print(summarize_library_trace(*args.summarize_library_trace, args.command), end="")
         return
     if args.summarize_trace or args.summarize_traffic:
         if args.summarize_trace:
@@ -497,11 +429,6 @@ def main():
     from convolution_forward_gemm_amd import binding as b
     from convolution_forward_gemm_amd import workloads as wl
 
-    if args.library_comparison:
-        for row in library_comparison(torch, b, wl):
-            print(json.dumps(row), flush=True)
-        return
-
     wk = wl.WORKLOADS[args.workload]
     conv, xd, wd, yd, host_inputs = setup(wk, torch, b)
     if args.config is not None:  # profiling another configuration; not the reported choice
@@ -513,6 +440,7 @@ def main():
         conv.run_ptr(xp, wp, yp, wk.alpha, stream)
 
     torch.cuda.synchronize()
+    ramp_ms, ramp_n = clock_ramp(torch, step, args.clock_ramp_ms)
     ms = time_device(torch, step, args.steps, args.warmup)
     ops = conv_ops(wk, conv.P, conv.Q)
     tops = ops / (ms * 1e-3) / 1e12
@@ -526,6 +454,8 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "clock_ramp_ms": round(ramp_ms, 1),
+        "clock_ramp_launches": ramp_n,
         "ms_per_step": round(ms, 6),
         "higher_is_better": True,
         "scaling": "weak",

@@ -80,7 +80,11 @@ typedef struct conv2d_fprop_desc_s *conv2d_fprop_desc_t;
 
 /* Validate a problem and choose its kernel configuration: the tuned
  * configuration of a per-shape table, else the one a cost model fitted to
- * configuration sweeps predicts fastest among those that can run it.
+ * configuration sweeps predicts fastest among those that can run it.  This is
+ * where the CUTLASS notebook "Best practices for reducing host-side latency"
+ * puts the work of its sections "Compile once, run many times" and "Bypassing
+ * checks for argument-Operator compatibility": every check and every choice
+ * happens here once, on the host, with no GPU call.
  *   out         receives the descriptor (set to NULL on error)
  *   N,C,H,W     input batch, channels, height, width        (> 0)
  *   K,R,S       output channels, filter height, filter width (> 0)
@@ -95,26 +99,48 @@ conv_status_t conv2d_fprop_desc_create(conv2d_fprop_desc_t *out, int N, int C,
                                        int stride_w, int dil_h, int dil_w,
                                        conv_dtype_t dtype, conv_layout_t layout);
 
-/* Release a descriptor.  NULL is accepted and ignored. */
+/* Release a descriptor.  NULL is accepted and ignored.  The descriptor is
+ * the library's counterpart of the compiled artifact of the CUTLASS notebook
+ * "Best practices for reducing host-side latency", section "Compile once, run
+ * many times": made once, reused by every run, released by the caller. */
 conv_status_t conv2d_fprop_desc_destroy(conv2d_fprop_desc_t desc);
 
-/* Output extents P (rows) and Q (columns) of a descriptor. */
+/* Output extents P (rows) and Q (columns) of a descriptor:
+ *   P = floor((H + 2*pad_h - dil_h*(R-1) - 1) / stride_h) + 1, Q likewise,
+ * the rule the first turn of the POPCORNBENCH "Kimi-K2.6 l1_p80" transcript
+ * derives (512 -> 508 rows and 512 -> 496 columns for its dilated 5x9
+ * problem).  P and Q must not be NULL (CONV_ERR_NULL). */
 conv_status_t conv2d_fprop_desc_get_output_dims(conv2d_fprop_desc_t desc,
                                                 int *P, int *Q);
 
 /* NUL-terminated text naming the chosen kernel configuration, truncated to
  * buf_size bytes: "config=<index> <name> tile=<ch>ch x <px>px grid=<work-
- * groups> lds=<bytes per workgroup> threads=<per workgroup>". */
+ * groups> lds=<bytes per workgroup> threads=<per workgroup>".  It reports the
+ * per-shape choice that the TVM BYOC CUTLASS integration (apache/tvm PR
+ * 9261) makes with its profiler, and that the torchao PR 1515 review holds
+ * to be necessary (kernel parameters tuned to the input shapes); the fields mirror
+ * the tile, warp and stage parameters listed in CUTLASS issue 2996, section
+ * "CUTLASS Kernel Configuration".  buf_size 0 writes nothing. */
 conv_status_t conv2d_fprop_desc_get_config(conv2d_fprop_desc_t desc, char *buf,
                                            size_t buf_size);
 
 /* Number of kernel configurations compiled for a dtype, and a replacement of
- * a descriptor's configuration by index (for sweeps).  Returns
- * CONV_ERR_UNSUPPORTED if that configuration cannot run the problem. */
+ * a descriptor's configuration by index.  These are the candidate set and
+ * the per-candidate trial of the profiler-based kernel selection in the TVM
+ * BYOC CUTLASS integration (apache/tvm PR 9261), used here by the sweep that
+ * builds the per-shape table.  set_config returns CONV_ERR_UNSUPPORTED, and
+ * leaves the descriptor unchanged, if that configuration cannot run the
+ * problem; num_configs returns 0 for an unknown dtype. */
 int conv2d_fprop_num_configs(conv_dtype_t dtype);
 conv_status_t conv2d_fprop_desc_set_config(conv2d_fprop_desc_t desc, int config);
 
-/* Enqueue one convolution on `stream`.
+/* Enqueue one convolution on `stream`: the operation of CUTLASS issue 2996,
+ * section "CUTLASS Kernel Configuration" (int8), or of the first turn of the
+ * "Kimi-K2.6 l1_p80" transcript (fp32), as stated at the top of this file.
+ * Following the CUTLASS notebook "Best practices for reducing host-side
+ * latency", section "Bypassing checks for argument-Operator compatibility",
+ * every problem check was done once by desc_create; run only checks the
+ * pointers (null, alignment, overlap) and launches one kernel.
  *   x     device input  (layout per the descriptor)
  *   w     device filter (layout per the descriptor)
  *   y     device output (layout per the descriptor); fully overwritten
@@ -162,10 +188,20 @@ conv_status_t conv2d_fprop_graph_launch(conv2d_fprop_graph_t graph,
                                         hipStream_t stream);
 conv_status_t conv2d_fprop_graph_destroy(conv2d_fprop_graph_t graph);
 
-/* Layout transforms (pure permutations, int8).  C must be a multiple of 32.
- * src and dst must not overlap; both 16-byte aligned.
+/* Layout transforms (pure permutations, int8) into and out of the
+ * interleaved layouts that CUTLASS issue 2996 names in section "CUTLASS
+ * Kernel Configuration" (cutlass::layout::TensorNCxHWx<32> for the
+ * activation and output, TensorCxRSKx<32> for the filter; the TensorRT kernel
+ * of section "TensorRT Kernel Name" reads the same activation layout,
+ * "nchw_vect_c_32").  The memory orders are the plainest reading of those
+ * names:
  *   NCHW [N][C][H][W]          <-> NCxHWx<32> [N][C/32][H][W][32]
- *   KCRS [K][C][R][S]          <-> CxRSKx<32> [C/32][R][S][K][32]        */
+ *   KCRS [K][C][R][S]          <-> CxRSKx<32> [C/32][R][S][K][32]
+ * src and dst are device pointers owned by the caller, must not overlap and
+ * must both be 16-byte aligned; C must be a multiple of 32 and the tensor
+ * under 2^31 bytes.  Errors: CONV_ERR_NULL, CONV_ERR_INVALID_SHAPE (a size
+ * <= 0), CONV_ERR_UNSUPPORTED (C % 32, size, overlap), CONV_ERR_MISALIGNED,
+ * CONV_ERR_HIP (launch failure).  Each call enqueues one kernel. */
 conv_status_t conv_nchw_to_nc32hw32_i8(const int8_t *src, int8_t *dst, int N,
                                        int C, int H, int W, hipStream_t stream);
 conv_status_t conv_nc32hw32_to_nchw_i8(const int8_t *src, int8_t *dst, int N,
@@ -175,7 +211,10 @@ conv_status_t conv_kcrs_to_c32rsk32_i8(const int8_t *src, int8_t *dst, int K,
 conv_status_t conv_c32rsk32_to_kcrs_i8(const int8_t *src, int8_t *dst, int K,
                                        int C, int R, int S, hipStream_t stream);
 
-/* Static description of a status code (never NULL). */
+/* Static description of a status code (never NULL).  Status codes, not
+ * exceptions, carry the outcome of the argument checks that the torchao PR
+ * 1515 review puts at the head of an operator (checks, then dispatch, then
+ * the kernel). */
 const char *conv_status_string(conv_status_t status);
 
 #ifdef __cplusplus

@@ -276,11 +276,19 @@ def test_run_ignores_an_earlier_pending_hip_error():
     x_il = b.nchw_to_nc32hw32(_dev(x))
     w_il = b.kcrs_to_c32rsk32(_dev(w))
     y = torch.full(conv.y_shape, 77, dtype=torch.int8, device="cuda")
+    hip.hipGetLastError.restype = ctypes.c_int
     torch.cuda.synchronize()
-    assert hip.hipSetDevice(4096) != 0  # hipErrorInvalidDevice, now pending
-    st = b.lib.conv2d_fprop_run(conv._h, x_il.data_ptr(), w_il.data_ptr(), y.data_ptr(),
-                                wk.alpha, torch.cuda.current_stream().cuda_stream)
+    pending = hip.hipSetDevice(4096)  # hipErrorInvalidDevice, now pending
+    try:
+        assert pending != 0
+        st = b.lib.conv2d_fprop_run(conv._h, x_il.data_ptr(), w_il.data_ptr(), y.data_ptr(),
+                                    wk.alpha, torch.cuda.current_stream().cuda_stream)
+    finally:
+        # the caller's error is still pending after run (run neither reported
+        # nor consumed it); consume it here so that later calls see none
+        left = hip.hipGetLastError()
     assert st == b.CONV_OK
+    assert left == pending
     torch.cuda.synchronize()
     _, ref = oracle_i8_il(x, w, wk.alpha, wk.pad, wk.stride, wk.dil)
     assert np.array_equal(y.cpu().numpy(), ref)

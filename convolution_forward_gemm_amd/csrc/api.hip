@@ -165,7 +165,16 @@ bool plan_halo(const conv2d_fprop_desc_s &d, const I8Config &c, int64_t M, I8Par
     const int64_t r = vrow(m1) - vrow(m0) + (int64_t)(d.R - 1) * d.dh + 1;
     if (r > rows) rows = r;
   }
-  if (c.pw > 0 && (WV > c.pw || d.dh != 1 || d.dw != 1)) return false;
+  if (c.kind == 2 && c.swz) {
+    // swizzled rows: a power-of-two pitch holding the row (its even and odd
+    // columns in separate halves at stride 2); any dilation (each lane keeps
+    // its per-tap offsets)
+    if (d.sw != 1 && d.sw != 2) return false;
+    const int64_t need = d.sw == 2 ? 2 * ((WV + 1) / 2) : WV;
+    if (need > c.pw) return false;
+  } else if (c.pw > 0 && (WV > c.pw || d.dh != 1 || d.dw != 1)) {
+    return false;
+  }
   const int64_t pitch = c.pw > 0 ? c.pw : WV;   // halo row pitch in LDS, pixels
   const int64_t dpp = (rows * pitch + 63) / 64;  // 1 KiB blocks per half-plane
   const int64_t hblk = 2 * dpp;
@@ -176,7 +185,10 @@ bool plan_halo(const conv2d_fprop_desc_s &d, const I8Config &c, int64_t M, I8Par
   if ((d.C / 32) % cps != 0) return false;
   const int64_t filt =
       c.kind == 1 || (c.kind == 2 && c.al) ? (int64_t)d.R * d.S * (c.bm / 32) * 1024 * cps : 0;
-  const int64_t stage = filt + hblk * 1024 * cps;
+  // a swizzled halo takes the space of every halo DMA slot of the
+  // configuration (a compile-time stage size); others only what they use
+  const int64_t halo_cap = c.kind == 2 && c.swz ? (int64_t)c.hj * c.nwaves * 1024 : hblk * 1024;
+  const int64_t stage = filt + halo_cap * cps;
   int64_t lds = c.ns * stage + 1024;
   // kind 2: the prologue stages the filter of taps 0..R*S-2 once in LDS, in
   // the last ring slot (first written at the end of stage 0) if it fits there
@@ -191,10 +203,12 @@ bool plan_halo(const conv2d_fprop_desc_s &d, const I8Config &c, int64_t M, I8Par
   p.HV = (int)HV;
   p.WV = (int)WV;
   p.halo_dpp = (int)dpp;
-  p.halo_bytes = (int)(hblk * 1024);
+  p.halo_bytes = (int)halo_cap;
   p.stage_bytes = (int)stage;
   p.lds_bytes = (int)lds;
   p.pro_off = (int)pro_off;
+  p.fd_hv = make_fastdiv((uint32_t)HV);
+  p.fd_wv = make_fastdiv((uint32_t)WV);
   return true;
 }
 
@@ -224,6 +238,12 @@ bool plan(conv2d_fprop_desc_s &d, int cfg) {
     p.ntaps = p.CB * p.RS;
     p.ph = d.ph; p.pw = d.pw; p.sh = d.sh; p.sw = d.sw; p.dh = d.dh; p.dw = d.dw;
     p.k_tiles = (int)kt;
+    p.P = d.P;
+    p.fd_q = make_fastdiv((uint32_t)d.Q);
+    p.fd_pq = make_fastdiv((uint32_t)(d.P * d.Q));
+    p.fd_kt = make_fastdiv((uint32_t)kt);
+    p.fd_sh = make_fastdiv((uint32_t)d.sh);
+    p.fd_hv = p.fd_wv = make_fastdiv(1u);
     p.x_bytes = (uint32_t)d.x_bytes;
     p.w_bytes = (uint32_t)d.w_bytes;
     p.y_bytes = (uint32_t)d.y_bytes;

@@ -32,6 +32,7 @@
 
 #include "common.hpp"
 #include "epilogue_i8.hpp"
+#include "halo_swizzle.hpp"
 #include "kernels.hpp"
 
 namespace convfprop {
@@ -292,7 +293,7 @@ conv_i8_halo_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ w,
 // stage st-1, which the barrier at the end of stage st-1 released), so the
 // wait at the end of stage st counts NS-2 whole batches.
 template <int WK, int WP, int FK, int FP, int R, int S, int NS, int HJ, int PW = 0,
-          int CPS = 1, int AL = 0>
+          int CPS = 1, int AL = 0, int SW = 0>
 struct HaloAdTile {
   static constexpr int NWAVES = WK * WP;
   static constexpr int THREADS = 64 * NWAVES;
@@ -319,14 +320,24 @@ struct HaloAdTile {
   static constexpr int WAITL = AL ? (NS - 2) * NB : (NS - 3) * HJ * CPS + TPS * FK;
   static_assert(NS >= 3, "the ring needs a stage being read, one landed and one in flight");
   static_assert(WAIT0 < 64 && WAITL < 64, "vmcnt counts at most 63 outstanding loads");
+  static_assert(!SW || (PW >= 16 && (PW & (PW - 1)) == 0),
+                "the swizzled halo rotates rows within a power-of-two pitch");
+  // Swizzled halo: every stage takes the ring slot space of the most halo
+  // DMA blocks the configuration issues (HB per channel block), so a slot's
+  // base is a compile-time constant and folds, with the lane's tap offset
+  // register, into the LDS read's immediate offset.
+  static constexpr int HB = HJ * NWAVES * 1024;
+  static constexpr int SB = CPS * HB + (AL ? FBLK * 1024 : 0);
+  static constexpr int UNROLL = (TPS % 2) ? (NS % 2 ? 2 * NS : NS) : NS;  // lcm(NS, parity)
+  static_assert(!SW || (NS - 1) * SB < 2 * 65536, "slot bases past 128 KiB");
 };
 
 template <int WK, int WP, int FK, int FP, int R, int S, int NS, int HJ, int PW, int CPS, int AL,
-          bool PC>
+          int SW, bool PC>
 __global__ void __launch_bounds__(64 * WK * WP)
 conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ w,
                        int8_t *__restrict__ y, I8Params p) {
-  using T = HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL>;
+  using T = HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, SW>;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
 
   const int tid = threadIdx.x;
@@ -336,8 +347,8 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
   const int l32 = lane & 31;
 
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
-  const int ktile = tile % p.k_tiles;
-  const int mtile = tile / p.k_tiles;
+  const int mtile = fast_div(tile, p.fd_kt);
+  const int ktile = tile - mtile * p.k_tiles;
   const int k0 = ktile * T::BM;
   const int m0 = mtile * T::BN;
 
@@ -350,11 +361,13 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
   const int hblk = 2 * p.halo_dpp;
   unsigned char *dummy = lds + NS * p.stage_bytes;
 
-  const int n_first = m0 / p.PQ;
-  const int p_first = (m0 - n_first * p.PQ) / p.Q;
+  const int n_first = fast_div(m0, p.fd_pq);
+  const int p_first = fast_div(m0 - n_first * p.PQ, p.fd_q);
   const int v_lo = n_first * HV + p_first * p.sh;
 
   // ---- per-lane halo DMA sources (channel block 0) ------------------------
+  // Lane l of halo block g writes slot 64*g' + l of its half-plane; it loads
+  // the halo column that the layout puts in that slot.
   uint32_t hv_off[HJ];
   int hv_dst[HJ];
 #pragma unroll
@@ -365,13 +378,23 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
     if (g < hblk) {
       const int hp = g >= p.halo_dpp;
       const int slot = (g - hp * p.halo_dpp) * 64 + lane;
-      const int row = slot / WVL;
-      const int col = slot - row * WVL;
+      int row, col;
+      if constexpr (SW) {
+        row = slot / PW;
+      } else {
+        row = PW > 0 ? slot / PW : fast_div(slot, p.fd_wv);
+        col = slot - row * WVL;
+        if (col >= WV) col = -1;
+      }
       const int v = v_lo + row;
-      const int n = v / HV;
+      const int n = fast_div(v, p.fd_hv);
+      if constexpr (SW) {  // the row's rotation (halo_rot), then the inverse swizzle
+        const int rot = (p.Q * (n * p.P + fast_div(v - n * HV, p.fd_sh))) & 15;
+        col = halo_column_at(slot & (PW - 1), rot, p.sw, PW, WV);
+      }
       const int ih = v - n * HV - p.ph;
       const int iw = col - p.pw;
-      if (col < WV && n < p.N && (unsigned)ih < (unsigned)p.H && (unsigned)iw < (unsigned)p.W)
+      if (col >= 0 && n < p.N && (unsigned)ih < (unsigned)p.H && (unsigned)iw < (unsigned)p.W)
         off = (uint32_t)(((n * p.CB * p.H + ih) * p.W + iw) * 32 + hp * 16);
       dst = hp * plane + (g - hp * p.halo_dpp) * 1024;
     }
@@ -397,9 +420,9 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
     const int m = m0 + 32 * (wp * FP + i) + l32;
     int a = 0;
     if (m < p.M) {
-      const int n = m / p.PQ;
+      const int n = fast_div(m, p.fd_pq);
       const int pq = m - n * p.PQ;
-      const int op = pq / p.Q;
+      const int op = fast_div(pq, p.fd_q);
       const int oq = pq - op * p.Q;
       a = ((n * HV + op * p.sh - v_lo) * WVL + oq * p.sw) * 16;
     }
@@ -421,6 +444,16 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
 #pragma unroll
   for (int t = 0; t < T::RS; ++t)
     tap_off[t] = PW > 0 ? ((t / S) * PW + (t % S)) * 16 : ((t / S) * p.dh * WV + (t % S) * p.dw) * 16;
+  // Swizzled halo: a tap's slot is no fixed distance from the pixel's, so
+  // each lane keeps the LDS offset of every (fragment, tap) it reads.
+  int b_tap[SW ? FP : 1][SW ? T::RS : 1];  // filled after the first DMAs are out (below)
+  // LDS offset of fragment i at tap t of the stage (t < TPS) from the slot base
+  auto b_off = [&](int i, int t) __attribute__((always_inline)) -> int  {
+    if constexpr (SW)
+      return b_tap[i][t % T::RS] + (t / T::RS) * p.halo_bytes;
+    else
+      return b_addr_c[t / T::RS][i] + tap_off[t % T::RS];
+  };
 
   const int CB = p.CB;
   const int ntaps = CB * T::RS;
@@ -431,7 +464,7 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
 
   // AL = 1: the stage's filter follows its CPS halos; this wave's filter
   // DMA j carries block g = j*NWAVES + wave = t*KB + kb of the stage.
-  const int filt_off = CPS * p.halo_bytes;
+  const int filt_off = SW ? CPS * T::HB : CPS * p.halo_bytes;
   uint32_t fv_off[T::FJ > 0 ? T::FJ : 1];
 #pragma unroll
   for (int j = 0; j < T::FJ; ++j) {
@@ -440,7 +473,7 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
     fv_off[j] = g < T::FBLK && k < p.K ? (uint32_t)(k * 32 + 16 * half) : OOB_OFFSET;
   }
 
-  auto issue_stage = [&](int st) {
+  auto issue_stage = [&](int st) __attribute__((always_inline)) {
     unsigned char *base = lds + (st % NS) * p.stage_bytes;
     const bool live = st < NST;
 #pragma unroll
@@ -461,7 +494,7 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
   };
 
   // AL = 1: the d-th of the NB DMAs of stage st (halo blocks, then filter)
-  auto issue_dma = [&](int st, int d) {
+  auto issue_dma = [&](int st, int d) __attribute__((always_inline)) {
     unsigned char *base = lds + (st % NS) * p.stage_bytes;
     const bool live = st < NST;
     if (d < HJ * CPS) {
@@ -481,27 +514,54 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
   // Filter fragments of global tap g = cb*RS + t into a register slot; taps
   // past the end (prefetched, never used) re-read the last one.
   v4i aring[T::RS][FK];
-  auto load_a = [&](int g, v4i (&dst)[FK]) {
+  auto load_a = [&](int g, v4i (&dst)[FK]) __attribute__((always_inline)) {
     const int soff = (g < ntaps ? g : ntaps - 1) * KB32;
 #pragma unroll
     for (int i = 0; i < FK; ++i) dst[i] = load_b128_s(wr, a_off[i], soff);
   };
 
+  // Reads of stage st, held in ring slot K = st % NS.  slot_c is
+  // Slot<K> when K is known at compile time (the swizzled kernels' unrolled
+  // ring), else Slot<-1>.  With a compile-time K the slot base is an
+  // immediate: below 64 KiB it goes straight into the read's offset field;
+  // above, the lane's offset register carries 64 KiB (b_tap_hi) and the
+  // immediate the rest.
+  int b_tap_hi[SW ? FP : 1][SW ? T::RS : 1];
+  auto slot_base = [&](auto slot_c, int st) __attribute__((always_inline)) -> const unsigned char *  {
+    constexpr int K = decltype(slot_c)::value;
+    if constexpr (SW && K >= 0)
+      return lds + K * T::SB;
+    else
+      return lds + (st % NS) * p.stage_bytes;
+  };
   v4i af[2][FK];
-  auto read_a = [&](int st, int t, v4i (&a)[FK]) {  // AL = 1; t: tap within the stage
-    const unsigned char *base = lds + (st % NS) * p.stage_bytes + filt_off;
+  auto read_a = [&](auto slot_c, int st, int t, v4i (&a)[FK]) __attribute__((always_inline)) {  // AL = 1; t: tap within the stage
+    const unsigned char *base = slot_base(slot_c, st) + filt_off;
 #pragma unroll
     for (int i = 0; i < FK; ++i)
       a[i] = *reinterpret_cast<const v4i *>(base + ((t * T::KB + wk * FK + i) * 64 + lane) * 16);
   };
 
   v4i bf[2][FP];
-  auto read_b = [&](int st, int t, v4i (&b)[FP]) {  // t: tap within the stage
-    const unsigned char *base = lds + (st % NS) * p.stage_bytes;
+  auto read_b = [&](auto slot_c, int st, int t, v4i (&b)[FP]) __attribute__((always_inline)) {  // t: tap within the stage
+    constexpr int K = decltype(slot_c)::value;
+    if constexpr (SW && K >= 0 && K * T::SB >= 65536) {
+      const unsigned char *base = lds + K * T::SB - 65536;
 #pragma unroll
-    for (int i = 0; i < FP; ++i)
-      b[i] = *reinterpret_cast<const v4i *>(base + b_addr_c[t / T::RS][i] + tap_off[t % T::RS]);
+      for (int i = 0; i < FP; ++i)
+        b[i] = *reinterpret_cast<const v4i *>(base + b_tap_hi[i][t % T::RS] + (t / T::RS) * T::HB);
+    } else if constexpr (SW && K >= 0) {
+      const unsigned char *base = lds + K * T::SB;
+#pragma unroll
+      for (int i = 0; i < FP; ++i)
+        b[i] = *reinterpret_cast<const v4i *>(base + b_tap[i][t % T::RS] + (t / T::RS) * T::HB);
+    } else {
+      const unsigned char *base = slot_base(slot_c, st);
+#pragma unroll
+      for (int i = 0; i < FP; ++i) b[i] = *reinterpret_cast<const v4i *>(base + b_off(i, t));
+    }
   };
+  using RtSlot = std::integral_constant<int, -1>;
 
   v16i acc[FK][FP];
 #pragma unroll
@@ -526,13 +586,45 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
               ok && k < p.K ? (uint32_t)(k * 32 + 16 * half) : OOB_OFFSET, ok ? tap * KB32 : 0);
   }
   __builtin_amdgcn_sched_barrier(0);
+  // Swizzled halo: the lanes' tap offsets are worked out while stage 0's
+  // DMAs are in flight, off the path to their issue.
+  if constexpr (SW) {
+    int rdh_sh[R];  // floor(r * dh / sh), wave-uniform
+#pragma unroll
+    for (int r = 0; r < R; ++r) rdh_sh[r] = fast_div(r * p.dh, p.fd_sh);
+#pragma unroll
+    for (int i = 0; i < FP; ++i) {
+      int m = m0 + 32 * (wp * FP + i) + l32;
+      if (m >= p.M) m = m0;  // pixels past M read the tile's first pixel; never stored
+      const int n = fast_div(m, p.fd_pq);
+      const int pq = m - n * p.PQ;
+      const int op = fast_div(pq, p.fd_q);
+      const int oq = pq - op * p.Q;
+      const int vrel = n * HV + op * p.sh - v_lo;
+#pragma unroll
+      for (int t = 0; t < T::RS; ++t)
+        b_tap[i][t] = half * plane + 16 * halo_slot_of_pixel(vrel + (t / S) * p.dh,
+                                                             oq * p.sw + (t % S) * p.dw, m, oq,
+                                                             p.Q, rdh_sh[t / S], p.sw, PW);
+    }
+  }
+  if constexpr (SW && (NS - 1) * T::SB >= 65536) {  // some slot base needs it
+#pragma unroll
+    for (int i = 0; i < FP; ++i)
+#pragma unroll
+      for (int t = 0; t < T::RS; ++t) {
+        b_tap_hi[i][t] = b_tap[i][t] + 65536;
+        asm volatile("" : "+v"(b_tap_hi[i][t]));  // keep it a register of its own
+      }
+  }
+  __builtin_amdgcn_sched_barrier(0);
   halo_wait<T::WAIT0>();
   halo_barrier();
 #pragma unroll
   for (int s0 = 1; s0 < NS - 1; ++s0) issue_stage(s0);
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (AL) {
-    read_a(0, 0, af[0]);
+    read_a(std::integral_constant<int, 0>{}, 0, 0, af[0]);
   } else {
 #pragma unroll
     for (int g = 0; g < T::AHEAD; ++g)
@@ -540,10 +632,14 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
       for (int i = 0; i < FK; ++i)
         aring[g][i] = *reinterpret_cast<const v4i *>(apro + ((g * T::KB + wk * FK + i) * 64 + lane) * 16);
   }
-  read_b(0, 0, bf[0]);
+  read_b(std::integral_constant<int, 0>{}, 0, 0, bf[0]);
 
-  auto stage = [&](auto par_c, int st) {
+  // One ring stage; PAR is the fragment buffer of its tap 0 (the stage's
+  // taps may be odd), slot_c its ring slot (see read_b).
+  auto stage = [&](auto par_c, auto slot_c, int st) __attribute__((always_inline)) {
     constexpr int PAR = decltype(par_c)::value;
+    constexpr int KS = decltype(slot_c)::value;
+    using NextSlot = std::integral_constant<int, KS < 0 ? -1 : (KS + 1) % NS>;
 #pragma unroll
     for (int t = 0; t < T::TPS; ++t) {
       const int cur = (t + PAR) & 1;
@@ -559,16 +655,16 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
         }
       }
       if (t + 1 < T::TPS) {
-        if constexpr (AL) read_a(st, t + 1, af[nxt]);
-        read_b(st, t + 1, bf[nxt]);
+        if constexpr (AL) read_a(slot_c, st, t + 1, af[nxt]);
+        read_b(slot_c, st, t + 1, bf[nxt]);
       } else {
         __builtin_amdgcn_sched_barrier(0);
         halo_wait<T::WAITL>();
         halo_barrier();
         if constexpr (!AL) issue_stage(st + NS - 1);
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (AL) read_a(st + 1, 0, af[nxt]);
-        read_b(st + 1, 0, bf[nxt]);
+        if constexpr (AL) read_a(NextSlot{}, st + 1, 0, af[nxt]);
+        read_b(NextSlot{}, st + 1, 0, bf[nxt]);
       }
       // Pixel-fragment-major order: fragment b of this tap is done after its
       // FK MFMAs, and the next tap's fragment b is read into its registers
@@ -598,15 +694,33 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
   // With one channel block per stage the last stage runs apart (below); the
   // ring loop runs the others.
   const int NRING = CPS == 1 ? NST - 1 : NST;
-  if constexpr (T::TPS % 2 == 0) {
-    for (int st = 0; st < NRING; ++st) stage(Par0{}, st);
+  if constexpr (SW) {
+    // Unrolled over UNROLL = lcm(NS, tap parity) stages, so that every
+    // stage's ring slot and parity are compile-time constants; the remainder
+    // runs the same bodies behind a run-time guard.
+    int st = 0;
+    for (; st + T::UNROLL <= NRING; st += T::UNROLL) {
+      [&]<int... Ks>(std::integer_sequence<int, Ks...>) {
+        (stage(std::integral_constant<int, (T::TPS % 2) ? Ks % 2 : 0>{},
+               std::integral_constant<int, Ks % NS>{}, st + Ks),
+         ...);
+      }(std::make_integer_sequence<int, T::UNROLL>{});
+    }
+    [&]<int... Ks>(std::integer_sequence<int, Ks...>) {
+      ((st + Ks < NRING ? stage(std::integral_constant<int, (T::TPS % 2) ? Ks % 2 : 0>{},
+                                std::integral_constant<int, Ks % NS>{}, st + Ks)
+                        : void()),
+       ...);
+    }(std::make_integer_sequence<int, T::UNROLL - 1>{});
+  } else if constexpr (T::TPS % 2 == 0) {
+    for (int st = 0; st < NRING; ++st) stage(Par0{}, RtSlot{}, st);
   } else {
     int st = 0;
     for (; st + 1 < NRING; st += 2) {
-      stage(Par0{}, st);
-      stage(Par1{}, st + 1);
+      stage(Par0{}, RtSlot{}, st);
+      stage(Par1{}, RtSlot{}, st + 1);
     }
-    if (st < NRING) stage(Par0{}, st);
+    if (st < NRING) stage(Par0{}, RtSlot{}, st);
   }
 
   const int m_wave = m0 + 32 * wp * FP;
@@ -623,13 +737,13 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
 #pragma unroll
     for (int b = 0; b < FP; ++b) {
       v4i bb[2], aa[2][FK];
-      bb[0] = *reinterpret_cast<const v4i *>(base + b_addr_c[0][b] + tap_off[0]);
-      if constexpr (AL) read_a(st, 0, aa[0]);
+      bb[0] = *reinterpret_cast<const v4i *>(base + b_off(b, 0));
+      if constexpr (AL) read_a(RtSlot{}, st, 0, aa[0]);
 #pragma unroll
       for (int t = 0; t < T::RS; ++t) {
         if (t + 1 < T::RS) {
-          bb[(t + 1) & 1] = *reinterpret_cast<const v4i *>(base + b_addr_c[0][b] + tap_off[t + 1]);
-          if constexpr (AL) read_a(st, t + 1, aa[(t + 1) & 1]);
+          bb[(t + 1) & 1] = *reinterpret_cast<const v4i *>(base + b_off(b, t + 1));
+          if constexpr (AL) read_a(RtSlot{}, st, t + 1, aa[(t + 1) & 1]);
         }
 #pragma unroll
         for (int a = 0; a < FK; ++a)
@@ -647,24 +761,28 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
 }
 
 template <int WK, int WP, int FK, int FP, int R, int S, int NS, int HJ, int PW, int CPS, int AL,
-          bool PC>
+          int SW, bool PC>
 static hipError_t launch_i8_halo_ad_pc(const int8_t *x, const int8_t *w, int8_t *y,
                                        const I8Params &p, int grid, hipStream_t s) {
-  using T = HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL>;
+  using T = HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, SW>;
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void *>(&conv_i8_halo_ad_kernel<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, PC>),
+      reinterpret_cast<const void *>(
+          &conv_i8_halo_ad_kernel<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, SW, PC>),
       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   if (attr != hipSuccess) return attr;
-  return launch_kernel(&conv_i8_halo_ad_kernel<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, PC>, dim3(grid),
+  return launch_kernel(&conv_i8_halo_ad_kernel<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, SW, PC>,
+                       dim3(grid),
                      dim3(T::THREADS), p.lds_bytes, s, x, w, y, p);
 }
 
-template <int WK, int WP, int FK, int FP, int R, int S, int NS, int HJ, int PW, int CPS, int AL>
+template <int WK, int WP, int FK, int FP, int R, int S, int NS, int HJ, int PW, int CPS, int AL,
+          int SW>
 static hipError_t launch_i8_halo_ad(const int8_t *x, const int8_t *w, int8_t *y,
                                     const I8Params &p, int grid, hipStream_t s) {
-  return p.alpha_k
-             ? launch_i8_halo_ad_pc<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, true>(x, w, y, p, grid, s)
-             : launch_i8_halo_ad_pc<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, false>(x, w, y, p, grid, s);
+  return p.alpha_k ? launch_i8_halo_ad_pc<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, SW, true>(
+                         x, w, y, p, grid, s)
+                   : launch_i8_halo_ad_pc<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, SW, false>(
+                         x, w, y, p, grid, s);
 }
 
 template <int WK, int WP, int FK, int FP, int R, int S, int NS, int HJ, bool PC>
@@ -694,20 +812,25 @@ static hipError_t launch_i8_halo(const int8_t *x, const int8_t *w, int8_t *y,
         &launch_i8_halo<WK, WP, FK, FP, R, S, NS, HJ>, 1, R, S, WK * WP, NS, HJ        \
   }
 
-#define I8_HALO_AD_CFG_X(KINDNAME, WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL)          \
+#define I8_HALO_AD_CFG_X(KINDNAME, WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, SW, SUFFIX)  \
   I8Config {                                                                          \
     "i8_halo_" KINDNAME "_mfma32x32x32_wg" #WK "x" #WP "_frag" #FK "x" #FP "_r" #R "s" #S \
-    "_ring" #NS "_hj" #HJ "_pitch" #PW "_cps" #CPS,                                     \
-        HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL>::BM,                      \
-        HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL>::BN,                      \
-        HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL>::THREADS, 0, R * S, 0,    \
-        &launch_i8_halo_ad<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL>, 2, R, S, WK * WP, NS, \
-        HJ, PW, CPS, AL                                                               \
+    "_ring" #NS "_hj" #HJ "_pitch" #PW "_cps" #CPS SUFFIX,                              \
+        HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, SW>::BM,                  \
+        HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, SW>::BN,                  \
+        HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, SW>::THREADS, 0, R * S, 0, \
+        &launch_i8_halo_ad<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, SW>, 2, R, S, WK * WP, \
+        NS, HJ, PW, CPS, AL, SW                                                       \
   }
 #define I8_HALO_AD_CFG(WK, WP, FK, FP, R, S, NS, HJ, PW, CPS) \
-  I8_HALO_AD_CFG_X("regfilter", WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, 0)
+  I8_HALO_AD_CFG_X("regfilter", WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, 0, 0, "")
 #define I8_HALO_LF_CFG(WK, WP, FK, FP, R, S, NS, HJ, PW, CPS) \
-  I8_HALO_AD_CFG_X("ldsfilter", WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, 1)
+  I8_HALO_AD_CFG_X("ldsfilter", WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, 1, 0, "")
+// swizzled (bank-conflict-free) halo: PW is the power-of-two row pitch
+#define I8_HALO_AD_SWZ_CFG(WK, WP, FK, FP, R, S, NS, HJ, PW, CPS) \
+  I8_HALO_AD_CFG_X("regfilter", WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, 0, 1, "_swz")
+#define I8_HALO_LF_SWZ_CFG(WK, WP, FK, FP, R, S, NS, HJ, PW, CPS) \
+  I8_HALO_AD_CFG_X("ldsfilter", WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, 1, 1, "_swz")
 
 I8Config kI8HaloConfigs[] = {
     I8_HALO_CFG(2, 4, 2, 2, 3, 3, 3, 4),  // 128 ch x 256 px, 8 waves of 64x64
@@ -753,6 +876,12 @@ I8Config kI8HaloConfigs[] = {
     // the same with room for stride-2 halos (rows twice as far apart)
     I8_HALO_AD_CFG(2, 2, 1, 1, 3, 3, 3, 6, 64, 1),
     I8_HALO_AD_CFG(2, 2, 1, 2, 3, 3, 3, 9, 64, 1),
+    // swizzled halo rows (bank-conflict-free fragment reads at any tap, row
+    // wrap, image boundary; stride-2 columns split by parity)
+    I8_HALO_AD_SWZ_CFG(2, 4, 2, 2, 3, 3, 4, 2, 32, 1),   // 3x3 stride 1, like config 35
+    I8_HALO_AD_SWZ_CFG(2, 4, 2, 2, 3, 3, 3, 6, 64, 1),   // 3x3 stride 2, like config 37
+    I8_HALO_AD_SWZ_CFG(4, 2, 1, 4, 3, 3, 3, 6, 64, 1),   // stride 2, 32 x 128 per wave
+    I8_HALO_LF_SWZ_CFG(2, 4, 2, 2, 3, 3, 3, 2, 32, 1),   // filter in the ring, stride 1
 };
 int kNumI8HaloConfigs = sizeof(kI8HaloConfigs) / sizeof(kI8HaloConfigs[0]);
 

@@ -59,7 +59,7 @@ __device__ __forceinline__ uint32_t pack_low_bytes(uint32_t b0, uint32_t b1, uin
 // that their stores are dropped.  Adding kb * PQ * 32 moves to block kb.
 __device__ __forceinline__ uint32_t i8_pixel_yoff(const I8Params &p, int m, int half) {
   if (m >= p.M) return OOB_OFFSET;
-  const int n = m / p.PQ;
+  const int n = fast_div(m, p.fd_pq);
   const int pq = m - n * p.PQ;
   return (uint32_t)((n * p.KBLK * p.PQ + pq) * 32 + 16 * half);
 }

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fastdiv.hpp"
+
 namespace convfprop {
 
 // Problem constants of the int8 kernel, precomputed on the host once per
@@ -32,6 +34,10 @@ struct I8Params {
   int stage_bytes;   // filter taps + halo of one channel block
   int lds_bytes;     // dynamic LDS of one workgroup
   int pro_off;       // register-filter kernel: LDS offset of the prologue's filter taps
+  int P;             // output rows per image
+  // Division by the problem's extents in the halo kernels' prologues: by Q,
+  // P*Q, HV, k_tiles, WV and the vertical stride (see fastdiv.hpp).
+  FastDiv fd_q, fd_pq, fd_hv, fd_kt, fd_wv, fd_sh;
 };
 
 typedef hipError_t (*I8LaunchFn)(const int8_t *x, const int8_t *w, int8_t *y,
@@ -58,6 +64,7 @@ struct I8Config {
   int pw;   // kind 2: halo row pitch in LDS (0: the halo width; > 0: fixed, dilation 1)
   int cps;  // kind 2: channel blocks per ring stage (C/32 must be a multiple)
   int al;   // kind 2: 1 = filter taps in the LDS ring too, 0 = in registers
+  int swz;  // kind 2: 1 = swizzled halo rows (pitch pw, a power of two)
 };
 
 // Host-only tables (not const: a const namespace-scope object would also be

@@ -318,7 +318,9 @@ struct HaloAdTile {
   // stage NS-1 ahead (its slot was freed by the previous stage barrier)
   static constexpr int NB = HJ * CPS + FJ;
   static constexpr int WAITL = AL ? (NS - 2) * NB : (NS - 3) * HJ * CPS + TPS * FK;
-  static_assert(NS >= 3, "the ring needs a stage being read, one landed and one in flight");
+  static_assert(NS >= 3 || (AL && NS == 2),
+                "the ring needs a stage being read, one landed and one in flight (a two-slot "
+                "ring, filter in LDS only, issues a whole stage at the start of the one before)");
   static_assert(WAIT0 < 64 && WAITL < 64, "vmcnt counts at most 63 outstanding loads");
   static_assert(!SW || (PW >= 16 && (PW & (PW - 1)) == 0),
                 "the swizzled halo rotates rows within a power-of-two pitch");
@@ -646,8 +648,16 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
       const int nxt = (t + 1 + PAR) & 1;
       if constexpr (!AL) load_a(st * T::TPS + t + T::AHEAD, aring[(t + T::AHEAD) % T::RS]);
       if constexpr (AL) {
-        // this tap's share of stage st+NS-1's DMAs (the rest at the last tap)
-        if (t + 1 < T::TPS) {
+        if constexpr (NS == 2) {
+          // two slots: the next stage's slot was freed by the barrier that
+          // ended the previous stage; all its DMAs go out now and have the
+          // whole stage to land
+          if (t == 0) {
+#pragma unroll
+            for (int d = 0; d < T::NB; ++d) issue_dma(st + 1, d);
+          }
+        } else if (t + 1 < T::TPS) {
+          // this tap's share of stage st+NS-1's DMAs (the rest at the last tap)
           if (t < T::NB) issue_dma(st + NS - 1, t);
         } else {
 #pragma unroll
@@ -880,8 +890,9 @@ I8Config kI8HaloConfigs[] = {
     // wrap, image boundary; stride-2 columns split by parity)
     I8_HALO_AD_SWZ_CFG(2, 4, 2, 2, 3, 3, 4, 2, 32, 1),   // 3x3 stride 1, like config 35
     I8_HALO_AD_SWZ_CFG(2, 4, 2, 2, 3, 3, 3, 6, 64, 1),   // 3x3 stride 2, like config 37
-    I8_HALO_AD_SWZ_CFG(4, 2, 1, 4, 3, 3, 3, 6, 64, 1),   // stride 2, 32 x 128 per wave
-    I8_HALO_LF_SWZ_CFG(2, 4, 2, 2, 3, 3, 3, 2, 32, 1),   // filter in the ring, stride 1
+    // stride 2 with the filter in a two-slot ring (fetched once per
+    // workgroup; 2 x (42 KiB halo + 36 KiB filter) at pitch 57)
+    I8_HALO_LF_CFG(2, 4, 2, 2, 3, 3, 2, 6, 57, 1),
 };
 int kNumI8HaloConfigs = sizeof(kI8HaloConfigs) / sizeof(kI8HaloConfigs[0]);
 

@@ -243,6 +243,34 @@ __global__ void copy_kernel(const v4i *__restrict__ in, v4i *__restrict__ out, s
   for (; i < n; i += stride) out[i] = in[i];
 }
 
+// HBM streaming with enough bytes in flight: every thread issues U 16-byte
+// loads (coalesced across the grid: element i + u * stride) before its U
+// stores, non-temporal so the 256 MB Infinity Cache is not what is measured
+// (n is a multiple of U * stride).
+template <int U>
+__global__ void __launch_bounds__(256) copy_unrolled(const v4i *__restrict__ in,
+                                                     v4i *__restrict__ out, size_t n) {
+  const size_t stride = (size_t)gridDim.x * 256;
+  for (size_t i = blockIdx.x * (size_t)256 + threadIdx.x; i < n; i += U * stride) {
+    v4i v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(in + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < U; ++u) __builtin_nontemporal_store(v[u], out + i + u * stride);
+  }
+}
+template <int U>
+__global__ void __launch_bounds__(256) read_unrolled(const v4i *__restrict__ in, v4i *__restrict__ out,
+                                                     size_t n) {
+  const size_t stride = (size_t)gridDim.x * 256;
+  v4i acc = v4i{0, 0, 0, 0};
+  for (size_t i = blockIdx.x * (size_t)256 + threadIdx.x; i < n; i += U * stride) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= __builtin_nontemporal_load(in + i + u * stride);
+  }
+  if (acc[0] == 0x7fffffff && acc[1] == 0x13579) out[0] = acc;  // keeps the loads; never true here
+}
+
 int main() {
   setvbuf(stdout, nullptr, _IOLBF, 0);  // each line reaches a redirected log at once
   hipDeviceProp_t prop;
@@ -418,7 +446,31 @@ int main() {
   CHECK(hipEventRecord(e1));
   CHECK(hipEventSynchronize(e1));
   CHECK(hipEventElapsedTime(&ms, e0, e1));
-  printf("HBM copy 1 GiB (read + write)      : %8.1f GB/s\n", 5 * 2.0 * n * 16 / ms / 1e6);
+  printf("HBM copy 1 GiB (read + write)      : %8.1f GB/s  (one 16-byte load in flight per thread)\n",
+         5 * 2.0 * n * 16 / ms / 1e6);
+  {  // 8 loads in flight per thread, non-temporal; grid: 8 workgroups per CU
+    const int g = ncu * 8;
+    const size_t per = (size_t)g * 256 * 8;  // elements per pass of the grid
+    const size_t nn = n / per * per;
+    hipLaunchKernelGGL(copy_unrolled<8>, dim3(g), dim3(256), 0, 0, (const v4i *)a, (v4i *)b, nn);
+    CHECK(hipDeviceSynchronize());
+    CHECK(hipEventRecord(e0));
+    for (int r = 0; r < 5; ++r)
+      hipLaunchKernelGGL(copy_unrolled<8>, dim3(g), dim3(256), 0, 0, (const v4i *)a, (v4i *)b, nn);
+    CHECK(hipEventRecord(e1));
+    CHECK(hipEventSynchronize(e1));
+    CHECK(hipEventElapsedTime(&ms, e0, e1));
+    printf("HBM copy 1 GiB, 8 loads in flight   : %8.1f GB/s (read + write)\n", 5 * 2.0 * nn * 16 / ms / 1e6);
+    hipLaunchKernelGGL(read_unrolled<8>, dim3(g), dim3(256), 0, 0, (const v4i *)a, (v4i *)b, nn);
+    CHECK(hipDeviceSynchronize());
+    CHECK(hipEventRecord(e0));
+    for (int r = 0; r < 5; ++r)
+      hipLaunchKernelGGL(read_unrolled<8>, dim3(g), dim3(256), 0, 0, (const v4i *)a, (v4i *)b, nn);
+    CHECK(hipEventRecord(e1));
+    CHECK(hipEventSynchronize(e1));
+    CHECK(hipEventElapsedTime(&ms, e0, e1));
+    printf("HBM read 1 GiB, 8 loads in flight   : %8.1f GB/s\n", 5 * 1.0 * nn * 16 / ms / 1e6);
+  }
 
   // back-to-back launches on one stream, device time per launch
   for (int kind = 0; kind < 2; ++kind) {

@@ -29,14 +29,13 @@ PEAK_FP32_TFLOPS = 157.3     # MI355X fp32 MFMA
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 PROFILES = os.path.join(ROOT, "profiles")
 # every source that shapes the int8 kernels' code or launch
-KERNEL_SOURCES = ["convolution_forward_gemm_amd/csrc/conv_i8.hip",
-                  "convolution_forward_gemm_amd/csrc/conv_i8_halo.hip",
-                  "convolution_forward_gemm_amd/csrc/conv_i8_small.hip",
-                  "convolution_forward_gemm_amd/csrc/epilogue_i8.hpp",
-                  "convolution_forward_gemm_amd/csrc/kernels.hpp",
-                  "convolution_forward_gemm_amd/csrc/common.hpp",
-                  "convolution_forward_gemm_amd/csrc/api.hip",
-                  "convolution_forward_gemm_amd/build.py"]
+# Every source the library is built from: a counter summary whose hash no
+# longer matches was taken on other code and is not reported.
+KERNEL_SOURCES = sorted(
+    os.path.relpath(os.path.join(dp, fn), ROOT)
+    for dp, _, fns in os.walk(os.path.join(ROOT, "convolution_forward_gemm_amd", "csrc"))
+    for fn in fns if fn.endswith((".hip", ".hpp", ".inc", ".h"))
+) + ["convolution_forward_gemm_amd/build.py", "include/convfprop.h"]
 
 
 def traffic_file(key: str) -> str:
@@ -286,9 +285,15 @@ def summarize_trace(key, trace_dir, command, tag=""):
     conv = b.Conv2dFprop(wk.N, wk.C, wk.H, wk.W, wk.K, wk.R, wk.S, pad=wk.pad,
                          stride=wk.stride, dil=wk.dil, dtype=wk.dtype)
     ops = conv_ops(wk, conv.P, conv.Q)
-    lines += ["", "conv kernel average %.2f us -> %.1f TOPS = %.1f%% of the %.1f POP/s int8 MFMA peak"
-              % (avg / 1e3, ops / avg / 1e3, 100 * ops / avg / 1e3 / PEAK_INT8_TOPS, PEAK_INT8_TOPS / 1e3)]
-    out = os.path.join(PROFILES, "conv_i8_%s%s_kernel_trace.txt" % (key, tag))
+    if wk.dtype == "int8":
+        lines += ["", "conv kernel average %.2f us -> %.1f TOPS = %.1f%% of the %.1f POP/s int8 MFMA peak"
+                  % (avg / 1e3, ops / avg / 1e3, 100 * ops / avg / 1e3 / PEAK_INT8_TOPS,
+                     PEAK_INT8_TOPS / 1e3)]
+    else:
+        lines += ["", "conv kernel average %.2f us -> %.1f TFLOPS = %.1f%% of the %.1f TFLOPS fp32 MFMA peak"
+                  % (avg / 1e3, ops / avg / 1e3, 100 * ops / avg / 1e3 / PEAK_FP32_TFLOPS, PEAK_FP32_TFLOPS)]
+    prefix = "conv_i8" if wk.dtype == "int8" else "conv_f32"
+    out = os.path.join(PROFILES, "%s_%s%s_kernel_trace.txt" % (prefix, key, tag))
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     return out
@@ -369,7 +374,8 @@ def summarize_counters(key, dirs, commands, tag=""):
     lines += ["", "| counter | per dispatch | dispatches |", "|---|---|---|"]
     for c in sorted(acc):
         lines.append("| %s | %.1f | %d |" % (c, acc[c] / cnt[c], cnt[c]))
-    out = os.path.join(PROFILES, "conv_i8_%s%s_counters.md" % (key, tag))
+    prefix = "conv_i8" if wl.WORKLOADS[key].dtype == "int8" else "conv_f32"
+    out = os.path.join(PROFILES, "%s_%s%s_counters.md" % (prefix, key, tag))
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     return out

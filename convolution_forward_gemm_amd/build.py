@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libconvfprop.so")
 PEAK_PROBE = os.path.join(PKG, "peak_probe")
 SOURCES = ["api.hip", "conv_i8.hip", "conv_i8_halo.hip", "conv_i8_small.hip", "conv_f32.hip",
-           "transforms.hip"]
+           "conv_f32_halo.hip", "transforms.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

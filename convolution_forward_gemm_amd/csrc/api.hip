@@ -73,14 +73,26 @@ const I8Config *i8_config(int cfg) {
   return nullptr;
 }
 
+// fp32 configurations: the staged-weight kernels (and tiny ones), then the
+// row-halo kernels.
+int num_f32_configs() { return kNumF32Configs + kNumF32HaloConfigs; }
+
+const F32Config *f32_config(int cfg) {
+  if (cfg < 0) return nullptr;
+  if (cfg < kNumF32Configs) return &kF32Configs[cfg];
+  cfg -= kNumF32Configs;
+  if (cfg < kNumF32HaloConfigs) return &kF32HaloConfigs[cfg];
+  return nullptr;
+}
+
 // Index of the configuration with this name, or -1.
 int find_config(conv_dtype_t dtype, const char *name) {
   if (dtype == CONV_DTYPE_INT8) {
     for (int i = 0; i < num_i8_configs(); ++i)
       if (strcmp(i8_config(i)->name, name) == 0) return i;
   } else {
-    for (int i = 0; i < kNumF32Configs; ++i)
-      if (strcmp(kF32Configs[i].name, name) == 0) return i;
+    for (int i = 0; i < num_f32_configs(); ++i)
+      if (strcmp(f32_config(i)->name, name) == 0) return i;
   }
   return -1;
 }
@@ -112,11 +124,12 @@ const ShapeEntry kShapeTable[] = {
     // halo row pitch and a 3-stage ring
     {CONV_DTYPE_INT8, 32, 128, 56, 56, 256, 3, 3, 1, 1, 2, 2, 1, 1,
      "i8_halo_regfilter_mfma32x32x32_wg2x4_frag2x2_r3s3_ring3_hj6_pitch64_cps1"},
-    // fp32 5x9 dilated N8 C32 512x512 K64: 16 waves, 64 ch x 1024 px per
-    // workgroup (a quarter of a 4-wave tile's weight staging per pixel),
-    // the next channel chunk's weights staged while the current one runs
+    // fp32 5x9 dilated N8 C32 512x512 K64: one output row per workgroup, its
+    // five input rows and the weights of a channel pair staged in LDS, every
+    // tap's operand at an immediate offset; 8 waves of 64 ch x 64 px, one
+    // weight buffer (66 KB: two workgroups per CU)
     {CONV_DTYPE_FP32, 8, 32, 512, 512, 64, 5, 9, 2, 4, 1, 1, 2, 3,
-     "f32_mfma32x32x2_16waves_frag2x2_cc4_depth3_dbuf"},
+     "f32_rowhalo_mfma32x32x2_8waves_frag2x2_r5s9_dil2x3_pitch520_wsingle"},
 };
 
 int lookup_shape(const conv2d_fprop_desc_s &d) {
@@ -147,7 +160,8 @@ const SelectModel kSelectModel[] = {
 };
 
 int f32_lds_bytes(const conv2d_fprop_desc_s &d, int cfg) {
-  return kF32Configs[cfg].lds_bytes * d.R * d.S;
+  const F32Config &c = *f32_config(cfg);
+  return c.kind == 1 ? c.lds_bytes : c.lds_bytes * d.R * d.S;
 }
 
 
@@ -269,12 +283,23 @@ bool plan(conv2d_fprop_desc_s &d, int cfg) {
     }
     d.grid = (int)(mt * kt);
   } else {
-    if (cfg < 0 || cfg >= kNumF32Configs) return false;
-    const F32Config &c = kF32Configs[cfg];
+    const F32Config *cp = f32_config(cfg);
+    if (!cp) return false;
+    const F32Config &c = *cp;
     if (f32_lds_bytes(d, cfg) > 160 * 1024) return false;
     if (c.max_rs > 0 && d.R * d.S > c.max_rs) return false;
     if (c.nk > 0 && ((int64_t)d.C * d.R * d.S + 1) / 2 != c.nk) return false;
-    const int64_t mt = (M + c.bn - 1) / c.bn, kt = (d.K + c.bm - 1) / c.bm;
+    int64_t mt = (M + c.bn - 1) / c.bn;
+    const int64_t kt = (d.K + c.bm - 1) / c.bm;
+    if (c.kind == 1) {
+      // row halo: compiled filter size and dilation, a whole output row per
+      // workgroup, the taps of a row within the compiled row pitch
+      if (d.R != c.fr || d.S != c.fs || d.dh != c.fdh || d.dw != c.fdw) return false;
+      if (d.Q > c.bn) return false;
+      const int64_t wv = (int64_t)(d.Q - 1) * d.sw + (int64_t)(d.S - 1) * d.dw + 1;
+      if (wv > c.pitch) return false;
+      mt = (int64_t)d.N * d.P;  // one output row per workgroup
+    }
     if (mt * kt > 0x7fffffff) return false;
     F32Params &p = d.f32;
     p.M = (int)M;
@@ -292,6 +317,9 @@ bool plan(conv2d_fprop_desc_s &d, int cfg) {
     p.x_bytes = (uint32_t)d.x_bytes;
     p.w_bytes = (uint32_t)d.w_bytes;
     p.alpha = 1.0f;
+    p.P = d.P;
+    p.fd_kt = make_fastdiv((uint32_t)kt);
+    p.fd_p = make_fastdiv((uint32_t)d.P);
     d.grid = (int)(mt * kt);
   }
   d.config = cfg;
@@ -303,11 +331,11 @@ int desc_lds_bytes(const conv2d_fprop_desc_s &d) {
   return d.dtype == CONV_DTYPE_INT8 ? d.i8.lds_bytes : f32_lds_bytes(d, d.config);
 }
 int desc_threads(const conv2d_fprop_desc_s &d) {
-  return d.dtype == CONV_DTYPE_INT8 ? i8_config(d.config)->threads : kF32Configs[d.config].threads;
+  return d.dtype == CONV_DTYPE_INT8 ? i8_config(d.config)->threads : f32_config(d.config)->threads;
 }
 
 const char *config_name(conv_dtype_t dtype, int cfg) {
-  return dtype == CONV_DTYPE_INT8 ? i8_config(cfg)->name : kF32Configs[cfg].name;
+  return dtype == CONV_DTYPE_INT8 ? i8_config(cfg)->name : f32_config(cfg)->name;
 }
 
 // Predicted microseconds of a planned descriptor under its configuration's
@@ -322,8 +350,8 @@ double select_time(const conv2d_fprop_desc_s &d) {
     const int tlim = 2048 / threads > 1 ? 2048 / threads : 1;
     if (tlim < occ) occ = tlim;
     if (occ < 1) occ = 1;
-    const int bm = d.dtype == CONV_DTYPE_INT8 ? i8_config(d.config)->bm : kF32Configs[d.config].bm;
-    const int bn = d.dtype == CONV_DTYPE_INT8 ? i8_config(d.config)->bn : kF32Configs[d.config].bn;
+    const int bm = d.dtype == CONV_DTYPE_INT8 ? i8_config(d.config)->bm : f32_config(d.config)->bm;
+    const int bn = d.dtype == CONV_DTYPE_INT8 ? i8_config(d.config)->bn : f32_config(d.config)->bn;
     const double R = (double)((d.grid + 256 * occ - 1) / (256 * occ));
     const double crs = (double)d.C * d.R * d.S;
     const double W = (double)bm * bn * crs / 1e6, L = crs / 1e3;
@@ -337,7 +365,7 @@ double select_time(const conv2d_fprop_desc_s &d) {
 // The configuration with the least predicted time among those that plan for
 // the problem (earlier configurations win ties); false if none has a model.
 bool plan_by_model(conv2d_fprop_desc_s &d) {
-  const int n = d.dtype == CONV_DTYPE_INT8 ? num_i8_configs() : kNumF32Configs;
+  const int n = d.dtype == CONV_DTYPE_INT8 ? num_i8_configs() : num_f32_configs();
   int best = -1;
   double best_t = 0.0;
   for (int c = 0; c < n; ++c) {
@@ -418,7 +446,7 @@ conv_status_t conv2d_fprop_desc_create(conv2d_fprop_desc_t *out, int N, int C,
   if (cfg >= 0) ok = plan(*d, cfg);
   if (!ok) ok = plan_by_model(*d);
   if (!ok) {  // try every compiled configuration before giving up
-    const int n = dtype == CONV_DTYPE_INT8 ? num_i8_configs() : kNumF32Configs;
+    const int n = dtype == CONV_DTYPE_INT8 ? num_i8_configs() : num_f32_configs();
     for (int c = 0; c < n && !ok; ++c) ok = plan(*d, c);
   }
   if (!ok) {
@@ -445,9 +473,9 @@ conv_status_t conv2d_fprop_desc_get_config(conv2d_fprop_desc_t d, char *buf, siz
   if (!d || !buf) return CONV_ERR_NULL;
   if (n == 0) return CONV_OK;
   const bool i8 = d->dtype == CONV_DTYPE_INT8;
-  const char *name = i8 ? i8_config(d->config)->name : kF32Configs[d->config].name;
-  const int bm = i8 ? i8_config(d->config)->bm : kF32Configs[d->config].bm;
-  const int bn = i8 ? i8_config(d->config)->bn : kF32Configs[d->config].bn;
+  const char *name = i8 ? i8_config(d->config)->name : f32_config(d->config)->name;
+  const int bm = i8 ? i8_config(d->config)->bm : f32_config(d->config)->bm;
+  const int bn = i8 ? i8_config(d->config)->bn : f32_config(d->config)->bn;
   snprintf(buf, n, "config=%d %s tile=%dch x %dpx grid=%d lds=%d threads=%d", d->config, name,
            bm, bn, d->grid, desc_lds_bytes(*d), desc_threads(*d));
   return CONV_OK;
@@ -456,7 +484,7 @@ conv_status_t conv2d_fprop_desc_get_config(conv2d_fprop_desc_t d, char *buf, siz
 int conv2d_fprop_num_configs(conv_dtype_t dtype) {
   const int dt = enum_bits(dtype);
   if (dt == CONV_DTYPE_INT8) return num_i8_configs();
-  if (dt == CONV_DTYPE_FP32) return kNumF32Configs;
+  if (dt == CONV_DTYPE_FP32) return num_f32_configs();
   return 0;
 }
 
@@ -484,7 +512,7 @@ static conv_status_t run_impl(conv2d_fprop_desc_t d, const void *x, const void *
     p.alpha = alpha;
     p.alpha_k = alpha_k;
     p.bias_k = bias_k;
-    e = kF32Configs[d->config].launch((const float *)x, (const float *)w, (float *)y, p,
+    e = f32_config(d->config)->launch((const float *)x, (const float *)w, (float *)y, p,
                                       d->grid, stream);
   }
   return e == hipSuccess ? CONV_OK : CONV_ERR_HIP;

@@ -86,6 +86,8 @@ struct F32Params {
   uint32_t x_bytes, w_bytes;
   float alpha;
   const float *alpha_k, *bias_k;  // per-output-channel scale and bias, or null
+  int P;                          // output rows per image
+  FastDiv fd_kt, fd_p;            // division by k_tiles and by P (row-halo kernel)
 };
 
 typedef hipError_t (*F32LaunchFn)(const float *x, const float *w, float *y,
@@ -99,10 +101,14 @@ struct F32Config {
   F32LaunchFn launch;
   int nk;       // > 0: runs only problems of exactly nk MFMA steps,
                 // ceil(C*R*S / 2) (the unrolled tiny kernel)
+  int kind;     // 0: staged weights / direct activations, 1: row halo in LDS
+  int fr, fs, fdh, fdw, pitch;  // kind 1: compiled filter size, dilation, row pitch
 };
 
 extern F32Config kF32Configs[];
 extern int kNumF32Configs;
+extern F32Config kF32HaloConfigs[];
+extern int kNumF32HaloConfigs;
 
 // Layout transforms (transforms.hip).
 hipError_t launch_nchw_to_nc32(const int8_t *src, int8_t *dst, int N, int C,

@@ -273,9 +273,9 @@ static hipError_t launch_f32_halo(const float *x, const float *w, float *y, cons
 F32Config kF32HaloConfigs[] = {
     // the transcript's 5x9 filter with dilation (2, 3): rows of up to 520
     // columns (a 512-wide output row's taps span 496 + 24 columns)
-    F32_HALO_CFG(2, 2, 8, 5, 9, 2, 3, 520, 1, ""),   // 64 ch x 512 px, 8 waves, 90 KB
-    // one weight buffer: 66 KB of LDS, two workgroups per CU
+    // one weight buffer: 66 KB of LDS, two workgroups per CU (the faster)
     F32_HALO_CFG(2, 2, 8, 5, 9, 2, 3, 520, 0, "_wsingle"),
+    F32_HALO_CFG(2, 2, 8, 5, 9, 2, 3, 520, 1, ""),   // 64 ch x 512 px, 8 waves, 90 KB
 };
 int kNumF32HaloConfigs = sizeof(kF32HaloConfigs) / sizeof(kF32HaloConfigs[0]);
 

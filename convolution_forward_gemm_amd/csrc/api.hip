@@ -117,9 +117,10 @@ const ShapeEntry kShapeTable[] = {
      "i8_tiny_unrolled_r1s1_cb4_mfma32x32x32_frag1x1"},
     // int8 3x3 N32 C256 28x28 K256: activation halo in LDS, swizzled rows of
     // pitch 32 (bank-conflict-free fragment reads), filter fragments in
-    // registers, 128 ch x 256 px tiles, 8 waves of 64x64
+    // registers, 128 ch x 224 px tiles (224 workgroups), 8 waves of 32
+    // channels with 4 + 3 pixel fragments per SIMD
     {CONV_DTYPE_INT8, 32, 256, 28, 28, 256, 3, 3, 1, 1, 1, 1, 1, 1,
-     "i8_halo_regfilter_mfma32x32x32_wg2x4_frag2x2_r3s3_ring4_hj2_pitch32_cps1_swz"},
+     "i8_halo_regfilter_mfma32x32x32_wg4x2_frag1x4_r3s3_ring4_hj2_pitch32_cps1_pt7_swz"},
     // int8 3x3 stride-2 N32 C128 56x56 K256: the same kernel with a 64-pixel
     // halo row pitch and a 3-stage ring
     {CONV_DTYPE_INT8, 32, 128, 56, 56, 256, 3, 3, 1, 1, 2, 2, 1, 1,

@@ -293,14 +293,22 @@ conv_i8_halo_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ w,
 // stage st-1, which the barrier at the end of stage st-1 released), so the
 // wait at the end of stage st counts NS-2 whole batches.
 template <int WK, int WP, int FK, int FP, int R, int S, int NS, int HJ, int PW = 0,
-          int CPS = 1, int AL = 0, int SW = 0>
+          int CPS = 1, int AL = 0, int SW = 0, int PT = 0>
 struct HaloAdTile {
   static constexpr int NWAVES = WK * WP;
   static constexpr int THREADS = 64 * NWAVES;
   static constexpr int KB = WK * FK;
   static constexpr int PB = WP * FP;
+  // Pixel fragments in the tile.  PT < WP*FP leaves the last wave column
+  // FPL < FP fragments: with WK = 4, WP = 2, FP = 4, PT = 7 the two waves of
+  // a SIMD (waves w and w+4) own 4 + 3 fragments of the same 32 channels,
+  // 7 blocks per SIMD for a 128 x 224 tile.
+  static constexpr int PTILE = PT ? PT : PB;
+  static constexpr int FPL = PTILE - FP * (WP - 1);
+  static_assert(FPL >= 1 && FPL <= FP, "only the last wave column may be short");
+  static_assert(PTILE == PB || CPS == 1, "a short wave column needs one channel block per stage");
   static constexpr int BM = 32 * KB;
-  static constexpr int BN = 32 * PB;
+  static constexpr int BN = 32 * PTILE;
   static constexpr int RS = R * S;
   static constexpr int AHEAD = RS - 1;
   static constexpr int TPS = RS * CPS;  // taps per stage
@@ -335,11 +343,11 @@ struct HaloAdTile {
 };
 
 template <int WK, int WP, int FK, int FP, int R, int S, int NS, int HJ, int PW, int CPS, int AL,
-          int SW, bool PC>
+          int SW, int PT, bool PC>
 __global__ void __launch_bounds__(64 * WK * WP)
 conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ w,
                        int8_t *__restrict__ y, I8Params p) {
-  using T = HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, SW>;
+  using T = HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, SW, PT>;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
 
   const int tid = threadIdx.x;
@@ -544,32 +552,27 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
       a[i] = *reinterpret_cast<const v4i *>(base + ((t * T::KB + wk * FK + i) * 64 + lane) * 16);
   };
 
-  v4i bf[2][FP];
-  auto read_b = [&](auto slot_c, int st, int t, v4i (&b)[FP]) __attribute__((always_inline)) {  // t: tap within the stage
+  // b: the wave's pixel fragments (FP, or FPL in a short wave column)
+  auto read_b = [&](auto slot_c, int st, int t, auto &b) __attribute__((always_inline)) {  // t: tap within the stage
     constexpr int K = decltype(slot_c)::value;
+    constexpr int NF = std::extent_v<std::remove_reference_t<decltype(b)>>;
     if constexpr (SW && K >= 0 && K * T::SB >= 65536) {
       const unsigned char *base = lds + K * T::SB - 65536;
 #pragma unroll
-      for (int i = 0; i < FP; ++i)
+      for (int i = 0; i < NF; ++i)
         b[i] = *reinterpret_cast<const v4i *>(base + b_tap_hi[i][t % T::RS] + (t / T::RS) * T::HB);
     } else if constexpr (SW && K >= 0) {
       const unsigned char *base = lds + K * T::SB;
 #pragma unroll
-      for (int i = 0; i < FP; ++i)
+      for (int i = 0; i < NF; ++i)
         b[i] = *reinterpret_cast<const v4i *>(base + b_tap[i][t % T::RS] + (t / T::RS) * T::HB);
     } else {
       const unsigned char *base = slot_base(slot_c, st);
 #pragma unroll
-      for (int i = 0; i < FP; ++i) b[i] = *reinterpret_cast<const v4i *>(base + b_off(i, t));
+      for (int i = 0; i < NF; ++i) b[i] = *reinterpret_cast<const v4i *>(base + b_off(i, t));
     }
   };
   using RtSlot = std::integral_constant<int, -1>;
-
-  v16i acc[FK][FP];
-#pragma unroll
-  for (int a = 0; a < FK; ++a)
-#pragma unroll
-    for (int b = 0; b < FP; ++b) acc[a][b] = v16i{0};
 
   // Prologue: stage 0's halo and the filter of taps 0..RS-2 (block
   // g = tap*KB + kb at pro_off + g KiB, the MFMA operand order), then the
@@ -634,6 +637,18 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
       for (int i = 0; i < FK; ++i)
         aring[g][i] = *reinterpret_cast<const v4i *>(apro + ((g * T::KB + wk * FK + i) * 64 + lane) * 16);
   }
+
+  // The main loop and the epilogue, for a wave of NF pixel fragments (FP, or
+  // FPL in the last wave column of a short tile; both run the same stages,
+  // waits and barriers).
+  auto body = [&](auto nf_c) __attribute__((always_inline)) {
+  constexpr int NF = decltype(nf_c)::value;
+  v16i acc[FK][NF];
+#pragma unroll
+  for (int a = 0; a < FK; ++a)
+#pragma unroll
+    for (int b = 0; b < NF; ++b) acc[a][b] = v16i{0};
+  v4i bf[2][NF];
   read_b(std::integral_constant<int, 0>{}, 0, 0, bf[0]);
 
   // One ring stage; PAR is the fragment buffer of its tap 0 (the stage's
@@ -680,13 +695,13 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
       // FK MFMAs, and the next tap's fragment b is read into its registers
       // right then, a whole tap ahead of its first use.
 #pragma unroll
-      for (int b = 0; b < FP; ++b)
+      for (int b = 0; b < NF; ++b)
 #pragma unroll
         for (int a = 0; a < FK; ++a)
           acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(AL ? af[cur][a] : aring[t % T::RS][a],
                                                             bf[cur][b], acc[a][b], 0, 0, 0);
 #pragma unroll
-      for (int b = 0; b < FP; ++b) {
+      for (int b = 0; b < NF; ++b) {
         __builtin_amdgcn_sched_group_barrier(0x008, FK, 0);  // fragment b's MFMAs
         if constexpr (AL) {
           // this tap's reads for the next: FP pixel and FK filter fragments
@@ -745,7 +760,7 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
     if constexpr (!AL) load_a(st * T::TPS + T::AHEAD, aring[T::AHEAD % T::RS]);
     const unsigned char *base = lds + (st % NS) * p.stage_bytes;
 #pragma unroll
-    for (int b = 0; b < FP; ++b) {
+    for (int b = 0; b < NF; ++b) {
       v4i bb[2], aa[2][FK];
       bb[0] = *reinterpret_cast<const v4i *>(base + b_off(b, 0));
       if constexpr (AL) read_a(RtSlot{}, st, 0, aa[0]);
@@ -766,32 +781,39 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
     halo_wait<0>();  // no LDS-DMA (of the ring's idle stages) may outlive the workgroup
   } else {
     halo_wait<0>();
-    store_i8_tile<PC, FK, FP>(acc, y, p, m_wave, kb_wave, lane);
+    store_i8_tile<PC, FK, NF>(acc, y, p, m_wave, kb_wave, lane);
   }
+  };  // body
+  if constexpr (T::FPL == FP)
+    body(std::integral_constant<int, FP>{});
+  else if (wp == WP - 1)
+    body(std::integral_constant<int, T::FPL>{});
+  else
+    body(std::integral_constant<int, FP>{});
 }
 
 template <int WK, int WP, int FK, int FP, int R, int S, int NS, int HJ, int PW, int CPS, int AL,
-          int SW, bool PC>
+          int SW, int PT, bool PC>
 static hipError_t launch_i8_halo_ad_pc(const int8_t *x, const int8_t *w, int8_t *y,
                                        const I8Params &p, int grid, hipStream_t s) {
-  using T = HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, SW>;
+  using T = HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, SW, PT>;
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void *>(
-          &conv_i8_halo_ad_kernel<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, SW, PC>),
+          &conv_i8_halo_ad_kernel<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, SW, PT, PC>),
       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   if (attr != hipSuccess) return attr;
-  return launch_kernel(&conv_i8_halo_ad_kernel<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, SW, PC>,
-                       dim3(grid),
-                     dim3(T::THREADS), p.lds_bytes, s, x, w, y, p);
+  return launch_kernel(
+      &conv_i8_halo_ad_kernel<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, SW, PT, PC>, dim3(grid),
+      dim3(T::THREADS), p.lds_bytes, s, x, w, y, p);
 }
 
 template <int WK, int WP, int FK, int FP, int R, int S, int NS, int HJ, int PW, int CPS, int AL,
-          int SW>
+          int SW, int PT>
 static hipError_t launch_i8_halo_ad(const int8_t *x, const int8_t *w, int8_t *y,
                                     const I8Params &p, int grid, hipStream_t s) {
-  return p.alpha_k ? launch_i8_halo_ad_pc<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, SW, true>(
+  return p.alpha_k ? launch_i8_halo_ad_pc<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, SW, PT, true>(
                          x, w, y, p, grid, s)
-                   : launch_i8_halo_ad_pc<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, SW, false>(
+                   : launch_i8_halo_ad_pc<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, SW, PT, false>(
                          x, w, y, p, grid, s);
 }
 
@@ -822,25 +844,28 @@ static hipError_t launch_i8_halo(const int8_t *x, const int8_t *w, int8_t *y,
         &launch_i8_halo<WK, WP, FK, FP, R, S, NS, HJ>, 1, R, S, WK * WP, NS, HJ        \
   }
 
-#define I8_HALO_AD_CFG_X(KINDNAME, WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, SW, SUFFIX)  \
+#define I8_HALO_AD_CFG_X(KINDNAME, WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, SW, PT, SUFFIX) \
   I8Config {                                                                          \
     "i8_halo_" KINDNAME "_mfma32x32x32_wg" #WK "x" #WP "_frag" #FK "x" #FP "_r" #R "s" #S \
     "_ring" #NS "_hj" #HJ "_pitch" #PW "_cps" #CPS SUFFIX,                              \
-        HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, SW>::BM,                  \
-        HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, SW>::BN,                  \
-        HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, SW>::THREADS, 0, R * S, 0, \
-        &launch_i8_halo_ad<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, SW>, 2, R, S, WK * WP, \
-        NS, HJ, PW, CPS, AL, SW                                                       \
+        HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, SW, PT>::BM,              \
+        HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, SW, PT>::BN,              \
+        HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, SW, PT>::THREADS, 0, R * S, 0, \
+        &launch_i8_halo_ad<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, SW, PT>, 2, R, S, \
+        WK * WP, NS, HJ, PW, CPS, AL, SW                                              \
   }
 #define I8_HALO_AD_CFG(WK, WP, FK, FP, R, S, NS, HJ, PW, CPS) \
-  I8_HALO_AD_CFG_X("regfilter", WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, 0, 0, "")
+  I8_HALO_AD_CFG_X("regfilter", WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, 0, 0, 0, "")
 #define I8_HALO_LF_CFG(WK, WP, FK, FP, R, S, NS, HJ, PW, CPS) \
-  I8_HALO_AD_CFG_X("ldsfilter", WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, 1, 0, "")
+  I8_HALO_AD_CFG_X("ldsfilter", WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, 1, 0, 0, "")
 // swizzled (bank-conflict-free) halo: PW is the power-of-two row pitch
 #define I8_HALO_AD_SWZ_CFG(WK, WP, FK, FP, R, S, NS, HJ, PW, CPS) \
-  I8_HALO_AD_CFG_X("regfilter", WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, 0, 1, "_swz")
+  I8_HALO_AD_CFG_X("regfilter", WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, 0, 1, 0, "_swz")
 #define I8_HALO_LF_SWZ_CFG(WK, WP, FK, FP, R, S, NS, HJ, PW, CPS) \
-  I8_HALO_AD_CFG_X("ldsfilter", WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, 1, 1, "_swz")
+  I8_HALO_AD_CFG_X("ldsfilter", WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, 1, 1, 0, "_swz")
+// tiles of PT pixel fragments (the last wave column short)
+#define I8_HALO_AD_PT_CFG(WK, WP, FK, FP, R, S, NS, HJ, PW, SW, PT, SUFFIX) \
+  I8_HALO_AD_CFG_X("regfilter", WK, WP, FK, FP, R, S, NS, HJ, PW, 1, 0, SW, PT, "_pt" #PT SUFFIX)
 
 I8Config kI8HaloConfigs[] = {
     I8_HALO_CFG(2, 4, 2, 2, 3, 3, 3, 4),  // 128 ch x 256 px, 8 waves of 64x64
@@ -893,6 +918,12 @@ I8Config kI8HaloConfigs[] = {
     // stride 2 with the filter in a two-slot ring (fetched once per
     // workgroup; 2 x (42 KiB halo + 36 KiB filter) at pitch 57)
     I8_HALO_LF_CFG(2, 4, 2, 2, 3, 3, 2, 6, 57, 1),
+    // 128 ch x 224 px: eight waves of 32 channels, 4 + 3 pixel fragments per
+    // SIMD (7 blocks where 128 x 256 tiles give 8; 224 workgroups for the
+    // 25088-pixel problems), each wave pulling one filter fragment per tap
+    I8_HALO_AD_PT_CFG(4, 2, 1, 4, 3, 3, 4, 2, 32, 1, 7, "_swz"),
+    I8_HALO_AD_PT_CFG(4, 2, 1, 4, 3, 3, 4, 2, 32, 0, 7, ""),
+    I8_HALO_AD_PT_CFG(4, 2, 1, 4, 3, 3, 3, 6, 64, 0, 7, ""),
 };
 int kNumI8HaloConfigs = sizeof(kI8HaloConfigs) / sizeof(kI8HaloConfigs[0]);
 

@@ -48,6 +48,14 @@ def test_strided_3x3(checker):
     assert frags == 784 * 9 and plain == 2 * frags  # the plain layout: every group
 
 
+def test_224_pixel_tiles(checker):
+    # 128 x 224 tiles (7 fragments): tiles start mid-image on both workloads
+    frags, _ = _check(checker, 32, 28, 28, 3, 3, 1, 1, 1, 1, 1, 1, 224, 32)
+    assert frags == 784 * 9
+    frags, _ = _check(checker, 32, 56, 56, 3, 3, 1, 1, 2, 2, 1, 1, 224, 64)
+    assert frags == 784 * 9
+
+
 @pytest.mark.parametrize("seed", range(12))
 def test_random_shapes(checker, seed):
     r = np.random.default_rng(900 + seed)

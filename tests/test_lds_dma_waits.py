@@ -65,6 +65,20 @@ def _split(body):
     return body, []
 
 
+def _loops(body):
+    """Every (header index, loop lines) of the body, in text order."""
+    out = []
+    for i, line in enumerate(body):
+        m = re.match(r"^(\.LBB\w+):.*Loop Header", line)
+        if m:
+            label = m.group(1)
+            for j in range(i + 1, len(body)):
+                if re.match(r"^\s*s_c?branch\w*\s+%s\s*$" % re.escape(label), body[j]):
+                    out.append((i, body[i:j + 1]))
+                    break
+    return out
+
+
 def _events(lines):
     """Sequence of ('load', is_dma) and ('ringwait', n) events."""
     ev = []
@@ -128,6 +142,15 @@ def test_register_filter_kernels_ring_waits(halo_asm):
         # waves; with the filter in the LDS ring (AL) they are part of stage 0
         aj = 0 if ints[10] else ((r * s - 1) * wk * fk + wk * wp - 1) // (wk * wp)
         _check_kernel(name, body, ns, aj)
+        # A tile with a short last wave column runs its main loop twice over
+        # (full and short waves): both loops must issue the same loads and
+        # waits in the same order, so the check of the first covers both.
+        loops = [lp for _, lp in _loops(body) if any("v_mfma" in l for l in lp)]
+        pt = ints[12] if len(ints) > 12 else 0
+        if pt:
+            assert len(loops) == 2, (name, len(loops))
+        for lp in loops[1:]:
+            assert _events(lp) == _events(loops[0]), name
 
 
 def test_checker_catches_a_wait_that_is_too_loose():

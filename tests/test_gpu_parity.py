@@ -412,8 +412,10 @@ def test_f32_workload_c5_slabs():
     # Whole output slabs of the dilated 5x9 workload, element by element: all
     # 64 output channels over the first 16 and the last 16 output rows of the
     # first and the last image (2 x 64 x 32 x 496 = 2,031,616 outputs).  They
-    # hold complete 64-channel x 1024-pixel tiles of the chosen configuration,
-    # the top and bottom padding rows, and the ragged last tile of the output.
+    # hold 64 whole workgroup tiles of the chosen row-halo configuration (one
+    # output row of all 64 channels each, 496 of its 512 columns real), the
+    # rows whose taps reach into the top and bottom padding, and the output's
+    # last tile.
     wk = wl.WORKLOADS["c5"]
     _announce("fp32 workload c5 slabs", wk.name)
     x, w = wl.make_inputs(wk)

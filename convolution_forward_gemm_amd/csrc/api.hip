@@ -128,9 +128,9 @@ const ShapeEntry kShapeTable[] = {
     // fp32 5x9 dilated N8 C32 512x512 K64: one output row per workgroup, its
     // five input rows and the weights of a channel pair staged in LDS, every
     // tap's operand at an immediate offset; 8 waves of 64 ch x 64 px, one
-    // weight buffer (66 KB: two workgroups per CU)
+    // weight buffer (69 KB: two workgroups per CU), rows by 16-byte LDS-DMA
     {CONV_DTYPE_FP32, 8, 32, 512, 512, 64, 5, 9, 2, 4, 1, 1, 2, 3,
-     "f32_rowhalo_mfma32x32x2_8waves_frag2x2_r5s9_dil2x3_pitch520_wsingle"},
+     "f32_rowhalo_mfma32x32x2_8waves_frag2x2_r5s9_dil2x3_pitch520_wsingle_dma16"},
 };
 
 int lookup_shape(const conv2d_fprop_desc_s &d) {
@@ -299,6 +299,9 @@ bool plan(conv2d_fprop_desc_s &d, int cfg) {
       if (d.Q > c.bn) return false;
       const int64_t wv = (int64_t)(d.Q - 1) * d.sw + (int64_t)(d.S - 1) * d.dw + 1;
       if (wv > c.pitch) return false;
+      // 16-byte row DMA: whole 4-column quads in or out of the image, 16-byte
+      // aligned rows
+      if (c.dma16 && (d.pw % 4 != 0 || d.W % 4 != 0)) return false;
       mt = (int64_t)d.N * d.P;  // one output row per workgroup
     }
     if (mt * kt > 0x7fffffff) return false;

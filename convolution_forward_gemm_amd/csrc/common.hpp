@@ -55,6 +55,13 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, unsigned cha
                                            voff, __builtin_amdgcn_readfirstlane(soff), 0, 0);
 }
 
+// The same with 4 bytes per lane: 64 consecutive floats at dst.
+__device__ __forceinline__ void lds_dma4(__amdgpu_buffer_rsrc_t r, float *dst, uint32_t voff,
+                                         int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)dst, 4,
+                                           voff, __builtin_amdgcn_readfirstlane(soff), 0, 0);
+}
+
 // Launch-grid remap that keeps neighbouring logical tiles on one XCD.
 // Workgroups are dispatched round-robin over the 8 XCDs (wg b -> XCD b % 8),
 // each with its own L2.  XCD x runs wgs x, x+8, x+16, ...; this bijection

@@ -103,6 +103,7 @@ struct F32Config {
                 // ceil(C*R*S / 2) (the unrolled tiny kernel)
   int kind;     // 0: staged weights / direct activations, 1: row halo in LDS
   int fr, fs, fdh, fdw, pitch;  // kind 1: compiled filter size, dilation, row pitch
+  int dma16;    // kind 1: 16-byte row DMA (pw and W multiples of 4)
 };
 
 extern F32Config kF32Configs[];

@@ -337,6 +337,11 @@ F32_CASES = [
     (1, 3, 23, 21, 64, 5, 5, (2, 2), (2, 2), (1, 1)),
     (2, 3, 25, 40, 20, 5, 9, (2, 4), (1, 1), (2, 3)),
     (1, 3, 30, 30, 48, 7, 7, (3, 3), (2, 2), (1, 1)),
+    # the 5x9 dilated filter on shapes the 16-byte row DMA takes (pw and W
+    # multiples of 4, C even): several channel pairs, a partial channel
+    # tile, strides
+    (2, 6, 15, 36, 40, 5, 9, (2, 4), (1, 1), (2, 3)),
+    (3, 4, 21, 44, 64, 5, 9, (2, 4), (2, 2), (2, 3)),
 ]
 
 

@@ -128,7 +128,7 @@ const ShapeEntry kShapeTable[] = {
     // fp32 5x9 dilated N8 C32 512x512 K64: one output row per workgroup, its
     // five input rows and the weights of a channel pair staged in LDS, every
     // tap's operand at an immediate offset; 8 waves of 64 ch x 64 px, one
-    // weight buffer (69 KB: two workgroups per CU), rows by 16-byte LDS-DMA
+    // weight buffer (72 KB: two workgroups per CU), rows by 16-byte LDS-DMA
     {CONV_DTYPE_FP32, 8, 32, 512, 512, 64, 5, 9, 2, 4, 1, 1, 2, 3,
      "f32_rowhalo_mfma32x32x2_8waves_frag2x2_r5s9_dil2x3_pitch520_wsingle_dma16"},
 };

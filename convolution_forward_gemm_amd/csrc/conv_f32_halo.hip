@@ -22,7 +22,9 @@
 //         bytes per lane) or 4 bytes per lane, out-of-image lanes reading
 //         zeros through an out-of-range offset;
 //       - the pair's weights transposed to [channel of the pair][tap][k],
-//         loaded into registers a pair ahead and written to LDS.
+//         loaded into registers a pair ahead (eight threads per output
+//         channel, each element at a constant offset from the thread's
+//         base) and written to LDS.
 //     The tap (r, s) operand of pixel q is then at r*PITCH + q*sw + s*DW:
 //     the lane's pixel is its address register, the tap an immediate offset.
 //     The loop body is one LDS read per MFMA, no address arithmetic; the
@@ -34,8 +36,11 @@
 //     (WDB = 1) after one.
 //   * Bank-conflict-free reads: a plane (one channel) of rows or of weights
 //     is a multiple of 64 floats plus 32, so the two lane halves (channels c
-//     and c+1) read disjoint banks; weight tap rows are BM + 1 floats, so the
-//     transposing writes of consecutive taps spread over the banks.
+//     and c+1) read disjoint banks; weight tap rows are BM + 8 floats, so the
+//     transposing writes of a wave (8 channels x 8 taps) hit 64 banks.
+//   * Registers: 114-126 VGPRs, four waves per SIMD: two workgroups per CU
+//     (with one weight buffer), each hiding the other's staging and
+//     barriers.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -58,7 +63,10 @@ struct F32HaloTile {
   // 64 for BM = 64: the transposing writes of consecutive taps land on
   // consecutive banks) in channel planes of CIS floats (= 32 mod 64: the two
   // lane halves of an operand read hit disjoint banks)
-  static constexpr int KP = BM + 1;
+  // Eight threads per output channel stage its 2*RS weights; tap rows of
+  // BM + 8 floats put a wave's writes (eight channels, each thread's taps
+  // 8 apart) on 64 distinct banks.
+  static constexpr int KP = BM + 8;
   static constexpr int CIS = (RS * KP + 31) / 64 * 64 + 32 >= RS * KP ? (RS * KP + 31) / 64 * 64 + 32
                                                                      : (RS * KP + 31) / 64 * 64 + 96;
   static constexpr int WT = 2 * CIS;                          // floats: the pair's weights
@@ -69,7 +77,8 @@ struct F32HaloTile {
   static constexpr int DMA_BLOCKS = 2 * BPP;                  // per pair
   static constexpr int DJ = (DMA_BLOCKS + NW - 1) / NW;       // DMAs per wave per pair
   static constexpr int WELEM = BM * 2 * RS;                   // weights per pair
-  static constexpr int WJ = (WELEM + THREADS - 1) / THREADS;  // per thread
+  static constexpr int WJ = (2 * RS + 7) / 8;                 // weights per thread
+  static_assert(THREADS == 8 * BM, "eight threads per output channel");
   static_assert(PLANE >= BPP * DBLK && PLANE % 64 == 32, "plane pitch");
   static_assert(!D16 || PITCH % 4 == 0, "16-byte DMA blocks hold whole rows' quads");
   static_assert(CIS % 64 == 32 && CIS >= RS * KP, "weight channel plane pitch");
@@ -146,29 +155,37 @@ conv_f32_halo_kernel(const float *__restrict__ x, const float *__restrict__ w,
 
   // ---- weights of a pair: element e = kk * 2*RS + ci * RS + t of the
   // pair's contiguous run per output channel, into LDS [ci][t][kk] --------
+  // Thread tid stages output channel k0 + tid/8, elements part + 8j
+  // (part = tid % 8) of the pair's contiguous 2*RS-float run: one base
+  // offset per thread, the pair in the wave-uniform soffset, the element a
+  // constant.  (Spreading consecutive threads over consecutive elements
+  // instead needs a division per element and ~20 more VGPRs, which kept the
+  // kernel at three waves per SIMD: one workgroup per CU, 7% slower.)
   float wreg[T::WJ];
+  const int w_kk = tid >> 3, w_part = tid & 7;
+  const uint32_t w_base =
+      k0 + w_kk < p.K ? (uint32_t)(((k0 + w_kk) * p.C * T::RS + w_part) * 4) : OOB_OFFSET;
   auto load_w = [&](int pair) __attribute__((always_inline)) {
-    const int c0 = 2 * pair;
+    const int soff = __builtin_amdgcn_readfirstlane(2 * pair * T::RS * 4);
 #pragma unroll
-    for (int j = 0; j < T::WJ; ++j) {
-      const int e = j * T::THREADS + tid;
-      const int kk = e / (2 * T::RS);
-      const int rem = e - kk * (2 * T::RS);
-      const int ci = rem >= T::RS;
-      const bool ok = e < T::WELEM && k0 + kk < p.K && c0 + ci < p.C;
-      wreg[j] = load_f32(wr, ok ? (uint32_t)((((k0 + kk) * p.C + c0) * T::RS + rem) * 4) : OOB_OFFSET);
-    }
+    for (int j = 0; j < T::WJ; ++j)
+      wreg[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(wr, w_base + 32 * j, soff, 0));
   };
-  auto store_w = [&](float *wt) __attribute__((always_inline)) {
+  // into [ci][t][kk]; a second channel past C (odd C, last pair) is zero
+  auto store_w = [&](float *wt, int pair) __attribute__((always_inline)) {
+    const bool c1 = 2 * pair + 1 < p.C;
+    float *wb = wt + w_part * T::KP + w_kk;
 #pragma unroll
     for (int j = 0; j < T::WJ; ++j) {
-      const int e = j * T::THREADS + tid;
-      if (e < T::WELEM) {
-        const int kk = e / (2 * T::RS);
-        const int rem = e - kk * (2 * T::RS);
-        const int ci = rem >= T::RS;
-        const int t = rem - ci * T::RS;
-        wt[ci * T::CIS + t * T::KP + kk] = wreg[j];
+      const int lo = 8 * j;  // this element is tap lo + part of the run
+      if (lo + 7 < T::RS) {
+        wb[lo * T::KP] = wreg[j];
+      } else if (lo >= T::RS) {
+        if (w_part + lo < 2 * T::RS) wb[T::CIS + (lo - T::RS) * T::KP] = c1 ? wreg[j] : 0.0f;
+      } else if (w_part + lo < T::RS) {
+        wb[lo * T::KP] = wreg[j];
+      } else {
+        wb[T::CIS + (lo - T::RS) * T::KP] = c1 ? wreg[j] : 0.0f;
       }
     }
   };
@@ -191,7 +208,7 @@ conv_f32_halo_kernel(const float *__restrict__ x, const float *__restrict__ w,
   // prologue: pair 0 into row buffer 0 and weight buffer 0
   issue_act(0, lds);
   load_w(0);
-  store_w(lds + T::WOFF);
+  store_w(lds + T::WOFF, 0);
   __builtin_amdgcn_s_waitcnt(0);  // the LDS-DMAs of pair 0 (and every other count) done
   __syncthreads();
 
@@ -231,10 +248,10 @@ conv_f32_halo_kernel(const float *__restrict__ x, const float *__restrict__ w,
       __builtin_amdgcn_sched_group_barrier(0x008, FK * FP, 0);
     }
     if constexpr (WDB) {
-      if (more) store_w(wnxt);
+      if (more) store_w(wnxt, pair + 1);
     } else {
       __syncthreads();  // every wave is done with this pair's weights
-      if (more) store_w(wnxt);
+      if (more) store_w(wnxt, pair + 1);
     }
     __builtin_amdgcn_s_waitcnt(0);  // this wave's DMAs of the next pair have landed
     __syncthreads();
@@ -290,12 +307,12 @@ static hipError_t launch_f32_halo(const float *x, const float *w, float *y, cons
 F32Config kF32HaloConfigs[] = {
     // the transcript's 5x9 filter with dilation (2, 3): rows of up to 520
     // columns (a 512-wide output row's taps span 496 + 24 columns); one
-    // weight buffer (two workgroups per CU), rows by 16-byte LDS-DMA where
-    // the padding and width keep 4-column quads whole (the faster), else by
-    // 4-byte LDS-DMA
+    // weight buffer (72 KB, two workgroups per CU), rows by 16-byte LDS-DMA
+    // where the padding and width keep 4-column quads whole (the faster),
+    // else by 4-byte LDS-DMA
     F32_HALO_CFG(2, 2, 8, 5, 9, 2, 3, 520, 0, 1, "_wsingle_dma16"),
     F32_HALO_CFG(2, 2, 8, 5, 9, 2, 3, 520, 0, 0, "_wsingle"),
-    F32_HALO_CFG(2, 2, 8, 5, 9, 2, 3, 520, 1, 0, ""),   // two weight buffers, 90 KB
+    F32_HALO_CFG(2, 2, 8, 5, 9, 2, 3, 520, 1, 0, ""),   // two weight buffers, 98 KB
 };
 int kNumF32HaloConfigs = sizeof(kF32HaloConfigs) / sizeof(kF32HaloConfigs[0]);
 

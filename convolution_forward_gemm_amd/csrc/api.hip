@@ -192,9 +192,13 @@ bool plan_halo(const conv2d_fprop_desc_s &d, const I8Config &c, int64_t M, I8Par
     return false;
   }
   const int64_t pitch = c.pw > 0 ? c.pw : WV;   // halo row pitch in LDS, pixels
-  const int64_t dpp = (rows * pitch + 63) / 64;  // 1 KiB blocks per half-plane
+  // 1 KiB blocks per half-plane: of the LDS layout, or (halo through
+  // registers) of the row-major rows of WV pixels the loads bring
+  const int64_t dpp = c.rg ? (rows * WV + 63) / 64 : (rows * pitch + 63) / 64;
   const int64_t hblk = 2 * dpp;
   if ((hblk + c.nwaves - 1) / c.nwaves > c.hj) return false;
+  // registers: every row of the halo has its slots in half a ring slot
+  if (c.rg && rows * pitch > (int64_t)c.hj * c.nwaves * 32) return false;
   // kind 1 (and kind 2 with al) stages the filter taps of a stage's channel
   // blocks in LDS too; kind 2 otherwise keeps them in registers
   const int64_t cps = c.kind == 2 && c.cps > 1 ? c.cps : 1;
@@ -210,7 +214,9 @@ bool plan_halo(const conv2d_fprop_desc_s &d, const I8Config &c, int64_t M, I8Par
   // the last ring slot (first written at the end of stage 0) if it fits there
   const int64_t apro = c.kind == 2 && !c.al ? (int64_t)(d.R * d.S - 1) * (c.bm / 32) * 1024 : 0;
   int64_t pro_off = (c.ns - 1) * stage;
-  if (apro > stage) {
+  // (a halo through registers writes the next slot during the first stage,
+  // while slower waves may still copy the prologue filter out: its own space)
+  if (apro > stage || c.rg) {
     pro_off = lds;
     lds += apro;
   }

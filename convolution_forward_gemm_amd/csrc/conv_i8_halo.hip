@@ -293,7 +293,7 @@ conv_i8_halo_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ w,
 // stage st-1, which the barrier at the end of stage st-1 released), so the
 // wait at the end of stage st counts NS-2 whole batches.
 template <int WK, int WP, int FK, int FP, int R, int S, int NS, int HJ, int PW = 0,
-          int CPS = 1, int AL = 0, int SW = 0, int PT = 0>
+          int CPS = 1, int AL = 0, int SW = 0, int PT = 0, int RG = 0>
 struct HaloAdTile {
   static constexpr int NWAVES = WK * WP;
   static constexpr int THREADS = 64 * NWAVES;
@@ -326,9 +326,11 @@ struct HaloAdTile {
   // stage NS-1 ahead (its slot was freed by the previous stage barrier)
   static constexpr int NB = HJ * CPS + FJ;
   static constexpr int WAITL = AL ? (NS - 2) * NB : (NS - 3) * HJ * CPS + TPS * FK;
-  static_assert(NS >= 3 || (AL && NS == 2),
+  static_assert(NS >= 3 || (AL && NS == 2) || (RG && NS == 2),
                 "the ring needs a stage being read, one landed and one in flight (a two-slot "
-                "ring, filter in LDS only, issues a whole stage at the start of the one before)");
+                "ring, filter in LDS only, issues a whole stage at the start of the one before; "
+                "with the halo through registers, the registers hold the one in flight)");
+  static_assert(!RG || (SW && !AL && CPS == 1), "register-staged halo: swizzled, filter in registers");
   static_assert(WAIT0 < 64 && WAITL < 64, "vmcnt counts at most 63 outstanding loads");
   static_assert(!SW || (PW >= 16 && (PW & (PW - 1)) == 0),
                 "the swizzled halo rotates rows within a power-of-two pitch");
@@ -343,11 +345,11 @@ struct HaloAdTile {
 };
 
 template <int WK, int WP, int FK, int FP, int R, int S, int NS, int HJ, int PW, int CPS, int AL,
-          int SW, int PT, bool PC>
+          int SW, int PT, int RG, bool PC>
 __global__ void __launch_bounds__(64 * WK * WP)
 conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ w,
                        int8_t *__restrict__ y, I8Params p) {
-  using T = HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, SW, PT>;
+  using T = HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, SW, PT, RG>;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
 
   const int tid = threadIdx.x;
@@ -367,7 +369,9 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
 
   const int HV = p.HV, WV = p.WV;
   const int WVL = PW > 0 ? PW : WV;  // halo row pitch in LDS, pixels
-  const int plane = p.halo_dpp * 1024;
+  // half-plane offset in a ring slot (RG: half of the slot; p.halo_dpp then
+  // counts the row-major blocks the registers bring per half-plane)
+  const int plane = RG ? T::SB / 2 : p.halo_dpp * 1024;
   const int hblk = 2 * p.halo_dpp;
   unsigned char *dummy = lds + NS * p.stage_bytes;
 
@@ -385,6 +389,37 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
     const int g = j * T::NWAVES + wave;
     uint32_t off = OOB_OFFSET;
     int dst = -1;
+    if constexpr (RG) {
+      // register-staged halo: lane l of block g loads element
+      // q = 64 (g - hp*dpp) + l of its half-plane in row-major order (rows
+      // of WV columns: consecutive lanes, consecutive pixels) and later
+      // writes it to that element's swizzled slot; lanes past the slot's
+      // capacity write nothing
+      if (g < hblk) {
+        const int hp = g >= p.halo_dpp;
+        // (consecutive lanes take consecutive pixels: coalesced loads; at
+        // stride 2 an even and an odd column share an LDS bank, so the writes
+        // conflict two ways.  Giving each 16 lanes columns of one parity
+        // instead makes the writes conflict-free but the loads strided, and
+        // the kernel slower.)
+        const int q = (g - hp * p.halo_dpp) * 64 + lane;
+        const int row = fast_div(q, p.fd_wv);
+        const int col = q - row * WV;
+        if (row * PW < T::SB / 32) {
+          const int v = v_lo + row;
+          const int n = fast_div(v, p.fd_hv);
+          const int ih = v - n * HV - p.ph;
+          const int iw = col - p.pw;
+          if (n < p.N && (unsigned)ih < (unsigned)p.H && (unsigned)iw < (unsigned)p.W)
+            off = (uint32_t)(((n * p.CB * p.H + ih) * p.W + iw) * 32 + hp * 16);
+          const int rot = (p.Q * (n * p.P + fast_div(v - n * HV, p.fd_sh))) & 15;
+          dst = hp * plane + 16 * (row * PW + ((halo_split(col, p.sw, PW) + rot) & (PW - 1)));
+        }
+      }
+      hv_off[j] = off;
+      hv_dst[j] = dst;
+      continue;
+    }
     if (g < hblk) {
       const int hp = g >= p.halo_dpp;
       const int slot = (g - hp * p.halo_dpp) * 64 + lane;
@@ -503,6 +538,20 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
     }
   };
 
+  // RG = 1: stage st's halo into registers (coalesced 16-byte loads), and
+  // from registers into ring slot K (scattered 16-byte LDS writes)
+  v4i hreg[RG ? HJ : 1];
+  auto load_halo = [&](int st) __attribute__((always_inline)) {
+    const bool live = st < NST;
+#pragma unroll
+    for (int j = 0; j < HJ; ++j) hreg[j] = load_b128_s(xr, live ? hv_off[j] : OOB_OFFSET, live ? st * HW32 : 0);
+  };
+  auto write_halo = [&](int K) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < HJ; ++j)
+      if (hv_dst[j] >= 0) *reinterpret_cast<v4i *>(lds + K * T::SB + hv_dst[j]) = hreg[j];
+  };
+
   // AL = 1: the d-th of the NB DMAs of stage st (halo blocks, then filter)
   auto issue_dma = [&](int st, int d) __attribute__((always_inline)) {
     unsigned char *base = lds + (st % NS) * p.stage_bytes;
@@ -577,8 +626,12 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
   // Prologue: stage 0's halo and the filter of taps 0..RS-2 (block
   // g = tap*KB + kb at pro_off + g KiB, the MFMA operand order), then the
   // other stages once those have landed.  pro_off is a ring slot that is
-  // first written at the end of stage 0, or space of its own.
-  issue_stage(0);
+  // first written at the end of stage 0, or space of its own (always with
+  // the halo through registers, which writes the next slot during stage 0).
+  if constexpr (RG)
+    load_halo(0);
+  else
+    issue_stage(0);
   unsigned char *apro = lds + p.pro_off;
 #pragma unroll
   for (int j = 0; j < T::AJ; ++j) {  // AL = 0 only (AJ = 0 otherwise)
@@ -624,9 +677,17 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
   }
   __builtin_amdgcn_sched_barrier(0);
   halo_wait<T::WAIT0>();
+  if constexpr (RG) {
+    write_halo(0);
+    halo_wait<63>();  // the LDS writes
+  }
   halo_barrier();
+  if constexpr (RG) {
+    load_halo(1);
+  } else {
 #pragma unroll
-  for (int s0 = 1; s0 < NS - 1; ++s0) issue_stage(s0);
+    for (int s0 = 1; s0 < NS - 1; ++s0) issue_stage(s0);
+  }
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (AL) {
     read_a(std::integral_constant<int, 0>{}, 0, 0, af[0]);
@@ -662,6 +723,21 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
       const int cur = (t + PAR) & 1;
       const int nxt = (t + 1 + PAR) & 1;
       if constexpr (!AL) load_a(st * T::TPS + t + T::AHEAD, aring[(t + T::AHEAD) % T::RS]);
+      if constexpr (RG) {
+        // one register block of stage st+1 per tap into its slot (two slots:
+        // it held stage st-1, released by that stage's barrier), then its
+        // register reloaded with stage st+2's block; the compiler waits for
+        // each load (issued a stage earlier) before its write
+        constexpr int NEXT = KS >= 0 ? (KS + 1) % NS : -1;
+        static_assert(NS == 2, "register-staged halo: a two-slot ring");
+        if (t < HJ) {
+          const int j = t;
+          if (hv_dst[j] >= 0)
+            *reinterpret_cast<v4i *>(lds + (NEXT >= 0 ? NEXT : (st + 1) % NS) * T::SB + hv_dst[j]) = hreg[j];
+          const bool live = st + 2 < NST;
+          hreg[j] = load_b128_s(xr, live ? hv_off[j] : OOB_OFFSET, live ? (st + 2) * HW32 : 0);
+        }
+      }
       if constexpr (AL) {
         if constexpr (NS == 2) {
           // two slots: the next stage's slot was freed by the barrier that
@@ -684,9 +760,15 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
         read_b(slot_c, st, t + 1, bf[nxt]);
       } else {
         __builtin_amdgcn_sched_barrier(0);
-        halo_wait<T::WAITL>();
-        halo_barrier();
-        if constexpr (!AL) issue_stage(st + NS - 1);
+        if constexpr (RG) {
+          static_assert(!RG || HJ <= T::TPS, "one register block per tap");
+          halo_wait<63>();  // this stage's LDS writes (and reads) complete
+          halo_barrier();
+        } else {
+          halo_wait<T::WAITL>();
+          halo_barrier();
+          if constexpr (!AL) issue_stage(st + NS - 1);
+        }
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (AL) read_a(NextSlot{}, st + 1, 0, af[nxt]);
         read_b(NextSlot{}, st + 1, 0, bf[nxt]);
@@ -793,27 +875,27 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
 }
 
 template <int WK, int WP, int FK, int FP, int R, int S, int NS, int HJ, int PW, int CPS, int AL,
-          int SW, int PT, bool PC>
+          int SW, int PT, int RG, bool PC>
 static hipError_t launch_i8_halo_ad_pc(const int8_t *x, const int8_t *w, int8_t *y,
                                        const I8Params &p, int grid, hipStream_t s) {
-  using T = HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, SW, PT>;
+  using T = HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, SW, PT, RG>;
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void *>(
-          &conv_i8_halo_ad_kernel<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, SW, PT, PC>),
+          &conv_i8_halo_ad_kernel<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, SW, PT, RG, PC>),
       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   if (attr != hipSuccess) return attr;
   return launch_kernel(
-      &conv_i8_halo_ad_kernel<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, SW, PT, PC>, dim3(grid),
+      &conv_i8_halo_ad_kernel<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, SW, PT, RG, PC>, dim3(grid),
       dim3(T::THREADS), p.lds_bytes, s, x, w, y, p);
 }
 
 template <int WK, int WP, int FK, int FP, int R, int S, int NS, int HJ, int PW, int CPS, int AL,
-          int SW, int PT>
+          int SW, int PT, int RG>
 static hipError_t launch_i8_halo_ad(const int8_t *x, const int8_t *w, int8_t *y,
                                     const I8Params &p, int grid, hipStream_t s) {
-  return p.alpha_k ? launch_i8_halo_ad_pc<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, SW, PT, true>(
+  return p.alpha_k ? launch_i8_halo_ad_pc<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, SW, PT, RG, true>(
                          x, w, y, p, grid, s)
-                   : launch_i8_halo_ad_pc<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, SW, PT, false>(
+                   : launch_i8_halo_ad_pc<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, SW, PT, RG, false>(
                          x, w, y, p, grid, s);
 }
 
@@ -844,28 +926,32 @@ static hipError_t launch_i8_halo(const int8_t *x, const int8_t *w, int8_t *y,
         &launch_i8_halo<WK, WP, FK, FP, R, S, NS, HJ>, 1, R, S, WK * WP, NS, HJ        \
   }
 
-#define I8_HALO_AD_CFG_X(KINDNAME, WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, SW, PT, SUFFIX) \
+#define I8_HALO_AD_CFG_X(KINDNAME, WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, SW, PT, RG, SUFFIX) \
   I8Config {                                                                          \
     "i8_halo_" KINDNAME "_mfma32x32x32_wg" #WK "x" #WP "_frag" #FK "x" #FP "_r" #R "s" #S \
     "_ring" #NS "_hj" #HJ "_pitch" #PW "_cps" #CPS SUFFIX,                              \
-        HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, SW, PT>::BM,              \
-        HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, SW, PT>::BN,              \
-        HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, SW, PT>::THREADS, 0, R * S, 0, \
-        &launch_i8_halo_ad<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, SW, PT>, 2, R, S, \
-        WK * WP, NS, HJ, PW, CPS, AL, SW                                              \
+        HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, SW, PT, RG>::BM,              \
+        HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, SW, PT, RG>::BN,              \
+        HaloAdTile<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, SW, PT, RG>::THREADS, 0, R * S, 0, \
+        &launch_i8_halo_ad<WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, SW, PT, RG>, 2, R, S, \
+        WK * WP, NS, HJ, PW, CPS, AL, SW, RG                                              \
   }
 #define I8_HALO_AD_CFG(WK, WP, FK, FP, R, S, NS, HJ, PW, CPS) \
-  I8_HALO_AD_CFG_X("regfilter", WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, 0, 0, 0, "")
+  I8_HALO_AD_CFG_X("regfilter", WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, 0, 0, 0, 0, "")
 #define I8_HALO_LF_CFG(WK, WP, FK, FP, R, S, NS, HJ, PW, CPS) \
-  I8_HALO_AD_CFG_X("ldsfilter", WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, 1, 0, 0, "")
+  I8_HALO_AD_CFG_X("ldsfilter", WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, 1, 0, 0, 0, "")
 // swizzled (bank-conflict-free) halo: PW is the power-of-two row pitch
 #define I8_HALO_AD_SWZ_CFG(WK, WP, FK, FP, R, S, NS, HJ, PW, CPS) \
-  I8_HALO_AD_CFG_X("regfilter", WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, 0, 1, 0, "_swz")
+  I8_HALO_AD_CFG_X("regfilter", WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, 0, 1, 0, 0, "_swz")
 #define I8_HALO_LF_SWZ_CFG(WK, WP, FK, FP, R, S, NS, HJ, PW, CPS) \
-  I8_HALO_AD_CFG_X("ldsfilter", WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, 1, 1, 0, "_swz")
+  I8_HALO_AD_CFG_X("ldsfilter", WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, 1, 1, 0, 0, "_swz")
 // tiles of PT pixel fragments (the last wave column short)
 #define I8_HALO_AD_PT_CFG(WK, WP, FK, FP, R, S, NS, HJ, PW, SW, PT, SUFFIX) \
-  I8_HALO_AD_CFG_X("regfilter", WK, WP, FK, FP, R, S, NS, HJ, PW, 1, 0, SW, PT, "_pt" #PT SUFFIX)
+  I8_HALO_AD_CFG_X("regfilter", WK, WP, FK, FP, R, S, NS, HJ, PW, 1, 0, SW, PT, 0, "_pt" #PT SUFFIX)
+// swizzled halo through registers (stride-2 problems: the DMA form would
+// read every other pixel)
+#define I8_HALO_AD_RG_CFG(WK, WP, FK, FP, R, S, NS, HJ, PW, PT, SUFFIX) \
+  I8_HALO_AD_CFG_X("regfilter", WK, WP, FK, FP, R, S, NS, HJ, PW, 1, 0, 1, PT, 1, "_swz_rg" SUFFIX)
 
 I8Config kI8HaloConfigs[] = {
     I8_HALO_CFG(2, 4, 2, 2, 3, 3, 3, 4),  // 128 ch x 256 px, 8 waves of 64x64
@@ -924,6 +1010,9 @@ I8Config kI8HaloConfigs[] = {
     I8_HALO_AD_PT_CFG(4, 2, 1, 4, 3, 3, 4, 2, 32, 1, 7, "_swz"),
     I8_HALO_AD_PT_CFG(4, 2, 1, 4, 3, 3, 4, 2, 32, 0, 7, ""),
     I8_HALO_AD_PT_CFG(4, 2, 1, 4, 3, 3, 3, 6, 64, 0, 7, ""),
+    // stride 2 with the swizzled halo through registers: two LDS slots, the
+    // registers holding the stage in flight
+    I8_HALO_AD_RG_CFG(2, 4, 2, 2, 3, 3, 2, 6, 64, 0, ""),
 };
 int kNumI8HaloConfigs = sizeof(kI8HaloConfigs) / sizeof(kI8HaloConfigs[0]);
 

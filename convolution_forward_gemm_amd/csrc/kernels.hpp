@@ -65,6 +65,8 @@ struct I8Config {
   int cps;  // kind 2: channel blocks per ring stage (C/32 must be a multiple)
   int al;   // kind 2: 1 = filter taps in the LDS ring too, 0 = in registers
   int swz;  // kind 2: 1 = swizzled halo rows (pitch pw, a power of two)
+  int rg;   // kind 2 with swz: 1 = the halo comes through registers (coalesced
+            // row-major loads, scattered LDS writes), not LDS-DMA
 };
 
 // Host-only tables (not const: a const namespace-scope object would also be

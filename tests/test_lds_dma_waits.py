@@ -136,8 +136,15 @@ def test_register_filter_kernels_ring_waits(halo_asm):
     fns = _functions(halo_asm, "_ZN9convfprop22conv_i8_halo_ad_kernel")
     assert len(fns) >= 3
     for name, body in fns.items():
-        ints = _template_ints(name)  # <WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL>
+        ints = _template_ints(name)  # <WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, AL, SW, PT, RG>
         wk, wp, fk, _, r, s, ns = ints[:7]
+        if len(ints) > 13 and ints[13]:
+            # halo through registers: the ring has no LDS-DMA (the compiler
+            # places the waits for its ordinary loads); only the prologue's
+            # filter taps come by DMA, awaited in full before the first barrier
+            for _, lp in _loops(body):
+                assert not any(VMEM.match(l) and " lds" in l for l in lp), name
+            continue
         # the prologue's filter taps 0..R*S-2: (R*S-1)*WK*FK blocks over WK*WP
         # waves; with the filter in the LDS ring (AL) they are part of stage 0
         aj = 0 if ints[10] else ((r * s - 1) * wk * fk + wk * wp - 1) // (wk * wp)

@@ -454,10 +454,6 @@ conv_status_t conv2d_fprop_desc_create(conv2d_fprop_desc_t *out, int N, int C,
   bool ok = false;
   const int cfg = lookup_shape(*d);
   if (cfg >= 0) ok = plan(*d, cfg);
-  // fp32 kernels compiled for one filter size and dilation (no model entry):
-  // the first that plans for the problem's own filter is taken
-  for (int c = 0; !ok && dtype == CONV_DTYPE_FP32 && c < num_f32_configs(); ++c)
-    if (f32_config(c)->kind == 1) ok = plan(*d, c);
   if (!ok) ok = plan_by_model(*d);
   if (!ok) {  // try every compiled configuration before giving up
     const int n = dtype == CONV_DTYPE_INT8 ? num_i8_configs() : num_f32_configs();

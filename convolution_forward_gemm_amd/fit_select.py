@@ -201,9 +201,8 @@ def main():
              "command: " + a.command,
              "(per shape: measured time of the configuration the model predicts fastest, over the",
              " fastest measured; 'sweep-time default' is the configuration the library chose when",
-             " the sweep ran: for the kept data, the rule this model replaced, the least",
-             " rounds-times-tile-area candidate of a fixed list, except the first-layer fp32",
-             " shapes added later (12 training, 3 held-out), where it is the previous fit's pick)", ""]
+             " the sweep ran: the previous fit's pick, except the 189 short-reduction int8",
+             " training shapes added later, where it is this fit's pick before they were added)", ""]
     lines += summary_lines("training shapes:", ev_t) + [""]
     lines += summary_lines("held-out shapes:", ev_v) + [""]
     lines.append("held-out shapes, one by one (us: model's pick / fastest / sweep-time default):")

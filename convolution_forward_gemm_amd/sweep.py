@@ -266,6 +266,14 @@ def grid_shapes(kind):
                     for H, W in ((64, 64), (256, 256), (128, 200)):
                         for R, S, ph, pw, sh, sw, dh, dw in _FILTERS_F32:
                             out.append(("fp32", N, C, H, W, K, R, S, ph, pw, sh, sw, dh, dw))
+        # short reductions (C/32 * R * S from 3 to 27 taps): the tiny
+        # kernels' domain, one compiled configuration per tap count
+        for N in (4, 16, 48):
+            for K in (32, 160, 320):
+                for H, W in ((10, 10), (16, 40), (28, 28)):
+                    for C, f in ((32, 1), (32, 3), (96, 0), (96, 1), (192, 0), (288, 0), (384, 0)):
+                        R, S, ph, pw, sh, sw, dh, dw = _FILTERS_I8[f]
+                        out.append(("int8", N, C, H, W, K, R, S, ph, pw, sh, sw, dh, dw))
         # a network's first layer: 7x7 stride 2 on three channels
         for N in (1, 8, 32):
             for H in (112, 224):

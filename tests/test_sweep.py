@@ -55,7 +55,7 @@ def test_shape_grids_are_fixed_and_disjoint():
     # and no held-out shape may appear in the training grid
     train, val = sweep.grid_shapes("train"), sweep.grid_shapes("validate")
     assert train == sweep.grid_shapes("train") and val == sweep.grid_shapes("validate")
-    assert len(train) == 566 and len(val) == 46
+    assert len(train) == 755 and len(val) == 46
     # the only shared shape: 3x3 C256 at N = 4, also one GPU's share of the
     # batch-sharded N = 32 workload (the fit summary leaves it out of the
     # held-out figures)

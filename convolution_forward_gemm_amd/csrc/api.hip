@@ -185,7 +185,7 @@ bool plan_halo(const conv2d_fprop_desc_s &d, const I8Config &c, int64_t M, I8Par
     // swizzled rows: a power-of-two pitch holding the row (its even and odd
     // columns in separate halves at stride 2); any dilation (each lane keeps
     // its per-tap offsets)
-    if (d.sw != 1 && d.sw != 2) return false;
+    if (d.sw != c.swz) return false;  // compiled for one horizontal stride
     const int64_t need = d.sw == 2 ? 2 * ((WV + 1) / 2) : WV;
     if (need > c.pw) return false;
   } else if (c.pw > 0 && (WV > c.pw || d.dh != 1 || d.dw != 1)) {

@@ -35,6 +35,7 @@
 #include "halo_swizzle.hpp"
 #include "kernels.hpp"
 
+
 namespace convfprop {
 
 template <int WK, int WP, int FK, int FP, int R, int S, int NS, int HJ>
@@ -292,6 +293,9 @@ conv_i8_halo_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ w,
 // stage st+NS-1 go out one per tap during stage st (its ring slot held
 // stage st-1, which the barrier at the end of stage st-1 released), so the
 // wait at the end of stage st counts NS-2 whole batches.
+//
+// SW = 1 or 2 lays the halo out swizzled (halo_swizzle.hpp) for problems of
+// that horizontal stride; the layout's arithmetic is then straight-line code.
 template <int WK, int WP, int FK, int FP, int R, int S, int NS, int HJ, int PW = 0,
           int CPS = 1, int AL = 0, int SW = 0, int PT = 0, int RG = 0>
 struct HaloAdTile {
@@ -332,6 +336,7 @@ struct HaloAdTile {
                 "with the halo through registers, the registers hold the one in flight)");
   static_assert(!RG || (SW && !AL && CPS == 1), "register-staged halo: swizzled, filter in registers");
   static_assert(WAIT0 < 64 && WAITL < 64, "vmcnt counts at most 63 outstanding loads");
+  static_assert(SW >= 0 && SW <= 2, "swizzled halo for horizontal stride 1 or 2");
   static_assert(!SW || (PW >= 16 && (PW & (PW - 1)) == 0),
                 "the swizzled halo rotates rows within a power-of-two pitch");
   // Swizzled halo: every stage takes the ring slot space of the most halo
@@ -413,8 +418,31 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
           if (n < p.N && (unsigned)ih < (unsigned)p.H && (unsigned)iw < (unsigned)p.W)
             off = (uint32_t)(((n * p.CB * p.H + ih) * p.W + iw) * 32 + hp * 16);
           const int rot = (p.Q * (n * p.P + fast_div(v - n * HV, p.fd_sh))) & 15;
-          dst = hp * plane + 16 * (row * PW + ((halo_split(col, p.sw, PW) + rot) & (PW - 1)));
+          dst = hp * plane + 16 * (row * PW + ((halo_split(col, SW, PW) + rot) & (PW - 1)));
         }
+      }
+      hv_off[j] = off;
+      hv_dst[j] = dst;
+      continue;
+    }
+    if constexpr (PW == 64) {
+      // A block of 64 slots is one whole row: its image, bounds, base offset
+      // and rotation are the same for the whole wave (scalar work); a lane
+      // adds only its column.  (At pitch 32 a block holds two rows, and the
+      // per-lane form below times the same.)
+      if (g < hblk) {
+        const int hp = g >= p.halo_dpp;
+        const int gb = g - hp * p.halo_dpp;
+        const int v = v_lo + gb;
+        const int n = fast_div(v, p.fd_hv);
+        const int ih = v - n * HV - p.ph;
+        const bool row_ok = n < p.N && (unsigned)ih < (unsigned)p.H;
+        // + 32 * column gives the offset of input column (column - pad_w)
+        const uint32_t rbase = ((uint32_t)((n * p.CB * p.H + ih) * p.W) - (uint32_t)p.pw) * 32u + hp * 16;
+        const int rot = SW ? (p.Q * (n * p.P + fast_div(v - n * HV, p.fd_sh))) & 15 : 0;
+        const int col = SW ? halo_column_at(lane, rot, SW, PW, WV) : (lane < WV ? lane : -1);
+        if (col >= 0 && row_ok && (unsigned)(col - p.pw) < (unsigned)p.W) off = rbase + (uint32_t)col * 32u;
+        dst = hp * plane + gb * 1024;
       }
       hv_off[j] = off;
       hv_dst[j] = dst;
@@ -435,7 +463,7 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
       const int n = fast_div(v, p.fd_hv);
       if constexpr (SW) {  // the row's rotation (halo_rot), then the inverse swizzle
         const int rot = (p.Q * (n * p.P + fast_div(v - n * HV, p.fd_sh))) & 15;
-        col = halo_column_at(slot & (PW - 1), rot, p.sw, PW, WV);
+        col = halo_column_at(slot & (PW - 1), rot, SW, PW, WV);
       }
       const int ih = v - n * HV - p.ph;
       const int iw = col - p.pw;
@@ -659,11 +687,27 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
       const int op = fast_div(pq, p.fd_q);
       const int oq = pq - op * p.Q;
       const int vrel = n * HV + op * p.sh - v_lo;
+      if constexpr (SW == 1) {
+        // halo_slot_of_pixel at stride 1, term by term: row r's base (a
+        // multiple of 16 * PW, so the in-row part ORs in), the row's rotation
+        // from the lane's output-row start, then two operations per tap
+        const int rbase = half * plane + 16 * PW * vrel;
 #pragma unroll
-      for (int t = 0; t < T::RS; ++t)
-        b_tap[i][t] = half * plane + 16 * halo_slot_of_pixel(vrel + (t / S) * p.dh,
-                                                             oq * p.sw + (t % S) * p.dw, m, oq,
-                                                             p.Q, rdh_sh[t / S], p.sw, PW);
+        for (int r = 0; r < R; ++r) {
+          const int rot = (m - oq + p.Q * rdh_sh[r]) & 15;
+          const int w16 = (oq + rot) << 4;
+          const int base = rbase + 16 * PW * r * p.dh;
+#pragma unroll
+          for (int s = 0; s < S; ++s)
+            b_tap[i][r * S + s] = ((w16 + 16 * s * p.dw) & (16 * (PW - 1))) | base;
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < T::RS; ++t)
+          b_tap[i][t] = half * plane + 16 * halo_slot_of_pixel(vrel + (t / S) * p.dh,
+                                                               oq * SW + (t % S) * p.dw, m, oq,
+                                                               p.Q, rdh_sh[t / S], SW, PW);
+      }
     }
   }
   if constexpr (SW && (NS - 1) * T::SB >= 65536) {  // some slot base needs it
@@ -705,10 +749,6 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
   auto body = [&](auto nf_c) __attribute__((always_inline)) {
   constexpr int NF = decltype(nf_c)::value;
   v16i acc[FK][NF];
-#pragma unroll
-  for (int a = 0; a < FK; ++a)
-#pragma unroll
-    for (int b = 0; b < NF; ++b) acc[a][b] = v16i{0};
   v4i bf[2][NF];
   read_b(std::integral_constant<int, 0>{}, 0, 0, bf[0]);
 
@@ -801,6 +841,10 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
   // With one channel block per stage the last stage runs apart (below); the
   // ring loop runs the others.
   const int NRING = CPS == 1 ? NST - 1 : NST;
+#pragma unroll
+  for (int a = 0; a < FK; ++a)
+#pragma unroll
+    for (int b = 0; b < NF; ++b) acc[a][b] = v16i{0};
   if constexpr (SW) {
     // Unrolled over UNROLL = lcm(NS, tap parity) stages, so that every
     // stage's ring slot and parity are compile-time constants; the remainder
@@ -829,7 +873,6 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
     }
     if (st < NRING) stage(Par0{}, RtSlot{}, st);
   }
-
   const int m_wave = m0 + 32 * wp * FP;
   const int kb_wave = k0 / 32 + wk * FK;
   if constexpr (CPS == 1) {
@@ -941,17 +984,15 @@ static hipError_t launch_i8_halo(const int8_t *x, const int8_t *w, int8_t *y,
 #define I8_HALO_LF_CFG(WK, WP, FK, FP, R, S, NS, HJ, PW, CPS) \
   I8_HALO_AD_CFG_X("ldsfilter", WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, 1, 0, 0, 0, "")
 // swizzled (bank-conflict-free) halo: PW is the power-of-two row pitch
-#define I8_HALO_AD_SWZ_CFG(WK, WP, FK, FP, R, S, NS, HJ, PW, CPS) \
-  I8_HALO_AD_CFG_X("regfilter", WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, 0, 1, 0, 0, "_swz")
-#define I8_HALO_LF_SWZ_CFG(WK, WP, FK, FP, R, S, NS, HJ, PW, CPS) \
-  I8_HALO_AD_CFG_X("ldsfilter", WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, 1, 1, 0, 0, "_swz")
+#define I8_HALO_AD_SWZ_CFG(WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, SW) \
+  I8_HALO_AD_CFG_X("regfilter", WK, WP, FK, FP, R, S, NS, HJ, PW, CPS, 0, SW, 0, 0, "_swz")
 // tiles of PT pixel fragments (the last wave column short)
 #define I8_HALO_AD_PT_CFG(WK, WP, FK, FP, R, S, NS, HJ, PW, SW, PT, SUFFIX) \
   I8_HALO_AD_CFG_X("regfilter", WK, WP, FK, FP, R, S, NS, HJ, PW, 1, 0, SW, PT, 0, "_pt" #PT SUFFIX)
 // swizzled halo through registers (stride-2 problems: the DMA form would
 // read every other pixel)
 #define I8_HALO_AD_RG_CFG(WK, WP, FK, FP, R, S, NS, HJ, PW, PT, SUFFIX) \
-  I8_HALO_AD_CFG_X("regfilter", WK, WP, FK, FP, R, S, NS, HJ, PW, 1, 0, 1, PT, 1, "_swz_rg" SUFFIX)
+  I8_HALO_AD_CFG_X("regfilter", WK, WP, FK, FP, R, S, NS, HJ, PW, 1, 0, 2, PT, 1, "_swz_rg" SUFFIX)
 
 I8Config kI8HaloConfigs[] = {
     I8_HALO_CFG(2, 4, 2, 2, 3, 3, 3, 4),  // 128 ch x 256 px, 8 waves of 64x64
@@ -999,8 +1040,8 @@ I8Config kI8HaloConfigs[] = {
     I8_HALO_AD_CFG(2, 2, 1, 2, 3, 3, 3, 9, 64, 1),
     // swizzled halo rows (bank-conflict-free fragment reads at any tap, row
     // wrap, image boundary; stride-2 columns split by parity)
-    I8_HALO_AD_SWZ_CFG(2, 4, 2, 2, 3, 3, 4, 2, 32, 1),   // 3x3 stride 1, like config 35
-    I8_HALO_AD_SWZ_CFG(2, 4, 2, 2, 3, 3, 3, 6, 64, 1),   // 3x3 stride 2, like config 37
+    I8_HALO_AD_SWZ_CFG(2, 4, 2, 2, 3, 3, 4, 2, 32, 1, 1),   // 3x3 stride 1, like config 35
+    I8_HALO_AD_SWZ_CFG(2, 4, 2, 2, 3, 3, 3, 6, 64, 1, 2),   // 3x3 stride 2, like config 37
     // stride 2 with the filter in a two-slot ring (fetched once per
     // workgroup; 2 x (42 KiB halo + 36 KiB filter) at pitch 57)
     I8_HALO_LF_CFG(2, 4, 2, 2, 3, 3, 2, 6, 57, 1),

@@ -64,7 +64,8 @@ struct I8Config {
   int pw;   // kind 2: halo row pitch in LDS (0: the halo width; > 0: fixed, dilation 1)
   int cps;  // kind 2: channel blocks per ring stage (C/32 must be a multiple)
   int al;   // kind 2: 1 = filter taps in the LDS ring too, 0 = in registers
-  int swz;  // kind 2: 1 = swizzled halo rows (pitch pw, a power of two)
+  int swz;  // kind 2: swizzled halo rows (pitch pw, a power of two) for horizontal
+            // stride swz (1 or 2); 0 = row-major halo
   int rg;   // kind 2 with swz: 1 = the halo comes through registers (coalesced
             // row-major loads, scattered LDS writes), not LDS-DMA
 };

@@ -40,11 +40,12 @@ def _functions(asm, prefix):
             continue
         if cur is None:
             continue
-        body.append(line)
-        if re.match(r"^\s*s_endpgm", line):
+        if line.startswith(".Lfunc_end"):
             if cur.startswith(prefix):
                 out[cur] = body
             cur = None
+            continue
+        body.append(line)
     return out
 
 
@@ -53,15 +54,56 @@ def _template_ints(name):
 
 
 def _split(body):
-    """(prologue lines, loop-body lines): the body runs from the first loop
-    header label to the branch back to it."""
+    """(prologue lines, loop-body lines).  The prologue is the path from the
+    kernel's entry to the first loop header, walked in execution order: an
+    unconditional branch is followed; a conditional one is followed into a
+    loop header, or towards one when the fall-through path does not lead to
+    one (the compiler may place the loop after the epilogue), and otherwise
+    falls through.  The loop body runs from that header's label to
+    the branch back to it."""
+    labels, headers = {}, set()
     for i, line in enumerate(body):
-        m = re.match(r"^(\.LBB\w+):.*Loop Header", line)
+        m = re.match(r"^(\.LBB\w+):", line)
         if m:
+            labels[m.group(1)] = i
+            if "Loop Header" in line:
+                headers.add(m.group(1))
+    def reaches_header(k):
+        # straight-line code from line k (passing labels and conditional
+        # branches) arrives at a loop header
+        while k < len(body):
+            m = re.match(r"^(\.LBB\w+):", body[k])
+            if m and m.group(1) in headers:
+                return True
+            if re.match(r"^\s*(s_branch|s_endpgm|s_setpc)", body[k]):
+                return False
+            k += 1
+        return False
+
+    pro, i, steps = [], 0, 0
+    while i < len(body) and steps < 100000:
+        steps += 1
+        line = body[i]
+        m = re.match(r"^(\.LBB\w+):", line)
+        if m and m.group(1) in headers:
             label = m.group(1)
             for j in range(i + 1, len(body)):
                 if re.match(r"^\s*s_c?branch\w*\s+%s\s*$" % re.escape(label), body[j]):
-                    return body[:i], body[i:j + 1]
+                    return pro, body[i:j + 1]
+            return pro, []
+        m = re.match(r"^\s*s_branch\s+(\.LBB\w+)\s*$", line)
+        if m:
+            i = labels[m.group(1)]
+            continue
+        m = re.match(r"^\s*s_cbranch\w*\s+(\.LBB\w+)\s*$", line)
+        if m and (m.group(1) in headers or
+                  (not reaches_header(i + 1) and reaches_header(labels[m.group(1)]))):
+            i = labels[m.group(1)]
+            continue
+        if re.match(r"^\s*s_endpgm", line):
+            break
+        pro.append(line)
+        i += 1
     return body, []
 
 
@@ -93,15 +135,20 @@ def _events(lines):
     return ev
 
 
-def _check_kernel(name, body, ns, extra0=0):
+def _check_kernel(name, body, ns, extra0=0, batch=None):
     """extra0: DMAs that follow stage 0's batch in the prologue and must have
     landed at the first wait too (the register-filter kernel's prologue
-    filter taps)."""
+    filter taps).  batch: DMAs per wave per stage; by default the prologue
+    holds NS-1 whole batches (stages 0..NS-2), else it may also run the
+    first ring stages ahead of the loop (each issuing one batch more)."""
     pro, loop = _split(body)
     pro_ev, loop_ev = _events(pro), _events(loop)
     n_dma_pro = sum(1 for e in pro_ev if e == ("load", True))
-    assert (n_dma_pro - extra0) % (ns - 1) == 0, (name, n_dma_pro)
-    batch = (n_dma_pro - extra0) // (ns - 1)
+    if batch is None:
+        assert (n_dma_pro - extra0) % (ns - 1) == 0, (name, n_dma_pro)
+        batch = (n_dma_pro - extra0) // (ns - 1)
+    assert (n_dma_pro - extra0) % batch == 0 and n_dma_pro - extra0 >= (ns - 1) * batch, (
+        name, n_dma_pro)
     assert batch > 0, name
     assert loop_ev, "%s: no stage loop found" % name
     seq = []            # per load: DMA batch index or None
@@ -148,7 +195,11 @@ def test_register_filter_kernels_ring_waits(halo_asm):
         # the prologue's filter taps 0..R*S-2: (R*S-1)*WK*FK blocks over WK*WP
         # waves; with the filter in the LDS ring (AL) they are part of stage 0
         aj = 0 if ints[10] else ((r * s - 1) * wk * fk + wk * wp - 1) // (wk * wp)
-        _check_kernel(name, body, ns, aj)
+        # DMAs per wave per stage: the halo blocks of its CPS channel blocks,
+        # and with AL the filter blocks of its taps
+        hj, cps = ints[7], ints[9]
+        fj = ((r * s * cps) * (wk * fk) + wk * wp - 1) // (wk * wp) if ints[10] else 0
+        _check_kernel(name, body, ns, aj, batch=hj * cps + fj)
         # A tile with a short last wave column runs its main loop twice over
         # (full and short waves): both loops must issue the same loads and
         # waits in the same order, so the check of the first covers both.

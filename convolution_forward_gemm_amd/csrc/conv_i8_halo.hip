@@ -478,45 +478,14 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
   const int wk = wave % WK;
   const int wp = wave / WK;
 
-  // ---- per-lane filter fragment offsets (channels past K read zeros) ------
-  uint32_t a_off[FK];
-#pragma unroll
-  for (int i = 0; i < FK; ++i) {
-    const int k = k0 + 32 * (wk * FK + i) + l32;
-    a_off[i] = k < p.K ? (uint32_t)(k * 32 + 16 * half) : OOB_OFFSET;
-  }
-
-  // ---- per-lane pixel fragment addresses inside the halo -----------------
-  int b_addr[FP];
-#pragma unroll
-  for (int i = 0; i < FP; ++i) {
-    const int m = m0 + 32 * (wp * FP + i) + l32;
-    int a = 0;
-    if (m < p.M) {
-      const int n = fast_div(m, p.fd_pq);
-      const int pq = m - n * p.PQ;
-      const int op = fast_div(pq, p.fd_q);
-      const int oq = pq - op * p.Q;
-      a = ((n * HV + op * p.sh - v_lo) * WVL + oq * p.sw) * 16;
-    }
-    b_addr[i] = half * plane + a;
-  }
-  // output offsets of this wave's pixel fragments (decoded here, off the
-  // epilogue's critical path)
-  const __amdgpu_buffer_rsrc_t yr = make_rsrc(y, p.y_bytes);
-  uint32_t y_off[FP];
-#pragma unroll
-  for (int i = 0; i < FP; ++i) y_off[i] = i8_pixel_yoff(p, m0 + 32 * (wp * FP + i) + l32, half);
-  // the halo of the stage's c-th channel block sits c * halo_bytes further
-  int b_addr_c[CPS][FP];
-#pragma unroll
-  for (int c = 0; c < CPS; ++c)
-#pragma unroll
-    for (int i = 0; i < FP; ++i) b_addr_c[c][i] = b_addr[i] + c * p.halo_bytes;
+  // Per-lane operand and output offsets: declared here, worked out once
+  // stage 0's DMAs are out (below), so that the DMAs wait only for their own
+  // source offsets.
+  uint32_t a_off[FK];        // filter fragments (channels past K read zeros)
+  int b_addr_c[CPS][FP];     // pixel fragments in the halo, per channel block of a stage
   int tap_off[T::RS];
-#pragma unroll
-  for (int t = 0; t < T::RS; ++t)
-    tap_off[t] = PW > 0 ? ((t / S) * PW + (t % S)) * 16 : ((t / S) * p.dh * WV + (t % S) * p.dw) * 16;
+  uint32_t y_off[FP];        // output offsets of the wave's pixel fragments
+  const __amdgpu_buffer_rsrc_t yr = make_rsrc(y, p.y_bytes);
   // Swizzled halo: a tap's slot is no fixed distance from the pixel's, so
   // each lane keeps the LDS offset of every (fragment, tap) it reads.
   int b_tap[SW ? FP : 1][SW ? T::RS : 1];  // filled after the first DMAs are out (below)
@@ -672,6 +641,36 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
               ok && k < p.K ? (uint32_t)(k * 32 + 16 * half) : OOB_OFFSET, ok ? tap * KB32 : 0);
   }
   __builtin_amdgcn_sched_barrier(0);
+  // ---- per-lane filter fragment offsets --------------------------------
+#pragma unroll
+  for (int i = 0; i < FK; ++i) {
+    const int k = k0 + 32 * (wk * FK + i) + l32;
+    a_off[i] = k < p.K ? (uint32_t)(k * 32 + 16 * half) : OOB_OFFSET;
+  }
+  // ---- per-lane pixel fragment addresses inside the halo -----------------
+  if constexpr (!SW) {
+#pragma unroll
+    for (int i = 0; i < FP; ++i) {
+      const int m = m0 + 32 * (wp * FP + i) + l32;
+      int a = 0;
+      if (m < p.M) {
+        const int n = fast_div(m, p.fd_pq);
+        const int pq = m - n * p.PQ;
+        const int op = fast_div(pq, p.fd_q);
+        const int oq = pq - op * p.Q;
+        a = ((n * HV + op * p.sh - v_lo) * WVL + oq * p.sw) * 16;
+      }
+      // the halo of the stage's c-th channel block sits c * halo_bytes further
+#pragma unroll
+      for (int c = 0; c < CPS; ++c) b_addr_c[c][i] = half * plane + a + c * p.halo_bytes;
+    }
+#pragma unroll
+    for (int t = 0; t < T::RS; ++t)
+      tap_off[t] = PW > 0 ? ((t / S) * PW + (t % S)) * 16 : ((t / S) * p.dh * WV + (t % S) * p.dw) * 16;
+  }
+  // output offsets (decoded here, off the epilogue's critical path)
+#pragma unroll
+  for (int i = 0; i < FP; ++i) y_off[i] = i8_pixel_yoff(p, m0 + 32 * (wp * FP + i) + l32, half);
   // Swizzled halo: the lanes' tap offsets are worked out while stage 0's
   // DMAs are in flight, off the path to their issue.
   if constexpr (SW) {

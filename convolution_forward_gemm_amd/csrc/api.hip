@@ -122,9 +122,11 @@ const ShapeEntry kShapeTable[] = {
     {CONV_DTYPE_INT8, 32, 256, 28, 28, 256, 3, 3, 1, 1, 1, 1, 1, 1,
      "i8_halo_regfilter_mfma32x32x32_wg4x2_frag1x4_r3s3_ring4_hj2_pitch32_cps1_pt7_swz"},
     // int8 3x3 stride-2 N32 C128 56x56 K256: the same kernel with a 64-pixel
-    // halo row pitch and a 3-stage ring
+    // halo row pitch (one row per DMA block) and a 3-stage ring, 256 ch x
+    // 128 px tiles: all output channels in one workgroup, so each pixel
+    // tile's halo is fetched once, not once per 128-channel half
     {CONV_DTYPE_INT8, 32, 128, 56, 56, 256, 3, 3, 1, 1, 2, 2, 1, 1,
-     "i8_halo_regfilter_mfma32x32x32_wg2x4_frag2x2_r3s3_ring3_hj6_pitch64_cps1"},
+     "i8_halo_regfilter_mfma32x32x32_wg4x2_frag2x2_r3s3_ring3_hj4_pitch64_cps1"},
     // fp32 5x9 dilated N8 C32 512x512 K64: one output row per workgroup, its
     // five input rows and the weights of a channel pair staged in LDS, every
     // tap's operand at an immediate offset; 8 waves of 64 ch x 64 px, one

@@ -1053,6 +1053,10 @@ I8Config kI8HaloConfigs[] = {
     // stride 2 with the swizzled halo through registers: two LDS slots, the
     // registers holding the stage in flight
     I8_HALO_AD_RG_CFG(2, 4, 2, 2, 3, 3, 2, 6, 64, 0, ""),
+    // 256 ch x 128 px: every output channel of a K = 256 problem in one
+    // workgroup, so each pixel tile's halo is fetched once, not once per
+    // channel half (the same 64 x 64 waves and workgroup count)
+    I8_HALO_AD_CFG(4, 2, 2, 2, 3, 3, 3, 4, 64, 1),
 };
 int kNumI8HaloConfigs = sizeof(kI8HaloConfigs) / sizeof(kI8HaloConfigs[0]);
 

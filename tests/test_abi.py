@@ -223,7 +223,7 @@ def test_shape_table_choices(b):
         "c1": "i8_tiny_unrolled_r3s3_cb1_mfma32x32x32_frag1x1",
         "c2": "i8_tiny_unrolled_r1s1_cb4_mfma32x32x32_frag1x1",
         "c3": "i8_halo_regfilter_mfma32x32x32_wg4x2_frag1x4_r3s3_ring4_hj2_pitch32_cps1_pt7_swz",
-        "c4": "i8_halo_regfilter_mfma32x32x32_wg2x4_frag2x2_r3s3_ring3_hj6_pitch64_cps1",
+        "c4": "i8_halo_regfilter_mfma32x32x32_wg4x2_frag2x2_r3s3_ring3_hj4_pitch64_cps1",
         "c5": "f32_rowhalo_mfma32x32x2_8waves_frag2x2_r5s9_dil2x3_pitch520_wsingle_dma16",
     }
     for key, name in expect.items():

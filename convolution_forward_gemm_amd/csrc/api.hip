@@ -212,9 +212,11 @@ bool plan_halo(const conv2d_fprop_desc_s &d, const I8Config &c, int64_t M, I8Par
   const int64_t halo_cap = c.kind == 2 && c.swz ? (int64_t)c.hj * c.nwaves * 1024 : hblk * 1024;
   const int64_t stage = filt + halo_cap * cps;
   int64_t lds = c.ns * stage + 1024;
-  // kind 2: the prologue stages the filter of taps 0..R*S-2 once in LDS, in
-  // the last ring slot (first written at the end of stage 0) if it fits there
-  const int64_t apro = c.kind == 2 && !c.al ? (int64_t)(d.R * d.S - 1) * (c.bm / 32) * 1024 : 0;
+  // kind 2: the prologue stages the filter of its first halo_filter_ahead
+  // taps once in LDS, in the last ring slot (first written at the end of
+  // stage 0) if it fits there
+  const int64_t apro =
+      c.kind == 2 && !c.al ? (int64_t)halo_filter_ahead(d.R * d.S) * (c.bm / 32) * 1024 : 0;
   int64_t pro_off = (c.ns - 1) * stage;
   // (a halo through registers writes the next slot during the first stage,
   // while slower waves may still copy the prologue filter out: its own space)

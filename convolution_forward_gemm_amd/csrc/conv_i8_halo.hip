@@ -254,8 +254,8 @@ conv_i8_halo_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ w,
 // ---------------------------------------------------------------------------
 // Variant with the filter operand in registers.  Each wave loads its own
 // MFMA filter fragments straight from global memory (16 bytes per lane, the
-// MFMA operand order of CxRSKx<32>), RS-1 taps ahead, into a ring of RS
-// register slots; LDS holds only the activation halo.  This halves the LDS
+// MFMA operand order of CxRSKx<32>), AHEAD taps ahead (halo_filter_ahead),
+// into a ring of RS register slots; LDS holds only the activation halo.  This halves the LDS
 // bytes read per MFMA -- with 64-wide fragments LDS reads, not the matrix
 // unit, bound the all-LDS variant -- and shrinks a stage to the halo alone.
 //
@@ -264,7 +264,7 @@ conv_i8_halo_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ w,
 // that are certain to issue after that batch and before the wait.  The
 // compiler may move a filter load later (into the block that uses it) but
 // not earlier, so each count below is a lower bound under any such move:
-//   prologue (stage 0's halo batch and the filter of taps 0..RS-2, both
+//   prologue (stage 0's halo batch and the filter of taps 0..AHEAD-1, both
 //   by LDS-DMA; no register loads):
 //                             0                -> both have landed.  Stages
 //                             1..NS-2 are issued only after this wait, so at
@@ -314,10 +314,10 @@ struct HaloAdTile {
   static constexpr int BM = 32 * KB;
   static constexpr int BN = 32 * PTILE;
   static constexpr int RS = R * S;
-  static constexpr int AHEAD = RS - 1;
+  static constexpr int AHEAD = halo_filter_ahead(RS);
   static constexpr int TPS = RS * CPS;  // taps per stage
   static constexpr int WAIT0 = 0;
-  // The prologue brings the filter of taps 0..RS-2 into LDS once per
+  // The prologue brings the filter of taps 0..AHEAD-1 into LDS once per
   // workgroup (AHEAD*KB blocks of 1 KiB, AJ per wave) instead of once per
   // wave: the waves that share output channels would otherwise each load it.
   static constexpr int APRO_BLK = AHEAD * KB;
@@ -620,7 +620,7 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
   };
   using RtSlot = std::integral_constant<int, -1>;
 
-  // Prologue: stage 0's halo and the filter of taps 0..RS-2 (block
+  // Prologue: stage 0's halo and the filter of taps 0..AHEAD-1 (block
   // g = tap*KB + kb at pro_off + g KiB, the MFMA operand order), then the
   // other stages once those have landed.  pro_off is a ring slot that is
   // first written at the end of stage 0, or space of its own (always with
@@ -878,10 +878,13 @@ conv_i8_halo_ad_kernel(const int8_t *__restrict__ x, const int8_t *__restrict__ 
     // Last stage, pixel-fragment by pixel-fragment: once fragment b has all
     // its taps, its epilogue (vector ALU work and the store) overlaps the
     // MFMAs of fragment b+1.  The stage's halo landed at the previous
-    // stage's wait; the ring holds the filter of its taps 0..RS-2 and the
-    // last tap's is loaded here.
+    // stage's wait; the ring holds the filter of its taps 0..AHEAD-1 and the
+    // others are loaded here.
     const int st = NST - 1;
-    if constexpr (!AL) load_a(st * T::TPS + T::AHEAD, aring[T::AHEAD % T::RS]);
+    if constexpr (!AL) {
+#pragma unroll
+      for (int g = T::AHEAD; g < T::RS; ++g) load_a(st * T::TPS + g, aring[g % T::RS]);
+    }
     const unsigned char *base = lds + (st % NS) * p.stage_bytes;
 #pragma unroll
     for (int b = 0; b < NF; ++b) {

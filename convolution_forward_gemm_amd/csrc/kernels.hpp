@@ -9,6 +9,14 @@
 
 namespace convfprop {
 
+// Register-filter halo kernel: how many filter taps ahead of its use each
+// wave loads a tap's filter fragments.  The prologue stages that many taps
+// in LDS, once per workgroup, before the first MFMA; the kernel and the
+// planner (which sizes that LDS) share this count.  Four measured best on
+// the 3x3 workloads: a shorter prologue, and enough lead for the ring's loads
+// (eight, six, four, three, two and one were tried).
+__host__ __device__ constexpr int halo_filter_ahead(int rs) { return rs - 1 < 4 ? rs - 1 : 4; }
+
 // Problem constants of the int8 kernel, precomputed on the host once per
 // descriptor.  Byte counts are < 2^31 (checked at descriptor creation).
 struct I8Params {

@@ -192,9 +192,11 @@ def test_register_filter_kernels_ring_waits(halo_asm):
             for _, lp in _loops(body):
                 assert not any(VMEM.match(l) and " lds" in l for l in lp), name
             continue
-        # the prologue's filter taps 0..R*S-2: (R*S-1)*WK*FK blocks over WK*WP
-        # waves; with the filter in the LDS ring (AL) they are part of stage 0
-        aj = 0 if ints[10] else ((r * s - 1) * wk * fk + wk * wp - 1) // (wk * wp)
+        # the prologue's filter taps 0..A-1, A = min(R*S-1, 4) taps ahead (the
+        # kernel's halo_filter_ahead): A*WK*FK blocks over WK*WP waves; with
+        # the filter in the LDS ring (AL) they are part of stage 0
+        ahead = min(r * s - 1, 4)
+        aj = 0 if ints[10] else (ahead * wk * fk + wk * wp - 1) // (wk * wp)
         # DMAs per wave per stage: the halo blocks of its CPS channel blocks,
         # and with AL the filter blocks of its taps
         hj, cps = ints[7], ints[9]
